@@ -1,0 +1,270 @@
+/*
+ * flux3_dit — the FLUX.3 Image Klein denoiser transformer on AMD Instinct
+ * MI355X (gfx950): C ABI.
+ *
+ * Sources (cited by page title and section):
+ *   [blog]  "Welcome FLUX.3 Image Klein in Diffusers" (Hugging Face blog),
+ *           sections "Two stages", "Inside one block", "Every token gets its
+ *           own timestep", "Positions in four dimensions", "The denoising loop".
+ *   [issue] "[Feature] FLUX.3 Image Klein support #2142" (stable-diffusion.cpp
+ *           issue): the part/size table of the description and the comment's
+ *           subsections "Tensor names (distilled checkpoint)", "Structure
+ *           (from dit.py)", "Sampling (sampling.py, pipeline.py)".
+ *
+ * Conventions shared by every entry point
+ *   - bf16 values are passed as uint16_t bit patterns; fp32 as float.
+ *   - Matrices are row-major.  Weights keep the checkpoint's [out, in] shape,
+ *     so every projection is Y = X W^T.
+ *   - "device" pointers are HIP device memory owned by the caller; "host"
+ *     pointers are ordinary host memory owned by the caller.  The library
+ *     never frees or keeps a caller's pointer after a call returns.
+ *   - Device pointers must be 16-byte aligned; leading dimensions are in
+ *     elements and must be multiples of 8.
+ *   - Every call that takes a hipStream_t only enqueues work on that stream
+ *     (the null stream is allowed) and returns without synchronising.
+ *   - Errors: every int-returning call returns FLUX3_OK (0) or a FLUX3_E*
+ *     code and never aborts.  flux3_last_error() gives a message for the last
+ *     failing call of the calling thread.  On error nothing was enqueued,
+ *     except FLUX3_EHIP, which reports a HIP launch failure.
+ *   - Token order inside one sample is image, image_cond (every reference),
+ *     text.  Stage-2 results for a token do not depend on this order (the
+ *     attention has no mask and positions and modulation travel with the
+ *     token), see [blog] "Two stages" and [issue] "Structure".
+ */
+#ifndef FLUX3_DIT_H
+#define FLUX3_DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define FLUX3_OK 0
+#define FLUX3_EINVAL 1        /* bad argument: null pointer, bad size, misalignment */
+#define FLUX3_EUNSUPPORTED 2  /* a shape the kernels do not handle */
+#define FLUX3_EWORKSPACE 3    /* workspace missing or smaller than required */
+#define FLUX3_EHIP 4          /* a HIP call or kernel launch failed */
+
+/* ---- model constants ([issue] description table and "Tensor names") ---- */
+#define FLUX3_HIDDEN 3072     /* transformer width */
+#define FLUX3_HEADS 24
+#define FLUX3_HEAD_DIM 128
+#define FLUX3_MLP_HIDDEN 9216 /* mlp_ratio 3; mlp_in produces 2 x 9216 */
+#define FLUX3_LATENT_CH 128   /* one latent token = 32 VAE channels x 2x2 */
+#define FLUX3_TXT_FEAT 20480  /* 8 text-encoder layers x 2560 */
+#define FLUX3_TIME_DIM 256    /* sinusoidal timestep embedding width */
+#define FLUX3_MAX_SEG 8       /* at most this many modulation segments per call */
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* flux3_last_error(void);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int flux3_version(void);
+
+/* ---- a1: positions ------------------------------------------------------
+ * flux3_build_ids: position ids (t, h, w, l) of one sample, host only.
+ * [blog] "Positions in four dimensions" (table) and [issue] "Structure":
+ *   image token (row, col)      -> (0, 0.5*row, 0.5*col, 0)
+ *   reference k token (row,col) -> (0, 0.5*row, 0.5*col, -(k+1))
+ *   text token i                -> (0, 0, 0, i)
+ * rows/cols are 0-based token-grid indices, row-major; text index 0-based.
+ *   img_h, img_w : image token grid (>= 0 each)
+ *   n_refs       : number of references; ref_hw (host, [n_refs][2]) their grids
+ *   n_txt        : text tokens (>= 0)
+ *   ids          : host output [N][4] fp32, N = img_h*img_w + sum(ref) + n_txt;
+ *                  may be NULL to query N only
+ *   n_out        : host output, N
+ * Every id is an exact multiple of 1/2, so the fp32 values are exact.
+ */
+int flux3_build_ids(int img_h, int img_w, int n_refs, const int* ref_hw, int n_txt,
+                    float* ids, int* n_out);
+
+/* flux3_rope_table: per-token rotation table for the 4-axis RoPE, on device.
+ * Axis a (t, h, w, l) owns head dims 32a..32a+31; its pair j = dims
+ * (32a+2j, 32a+2j+1) is rotated by angle id_a * 10000^(-2j/32)
+ * ([issue] description table: 4 axes of 32, theta 10000).
+ *   ids   : device [n][4] fp32 (from flux3_build_ids)
+ *   table : device output [n][64][2] fp32 = (cos, sin) per pair p = 16a + j;
+ *           angles and sin/cos are evaluated in fp64, then rounded to fp32
+ */
+int flux3_rope_table(const float* ids, int n, float* table, hipStream_t stream);
+
+/* ---- a2: modulation --------------------------------------------------------
+ * (shift, scale, gate) = chunk3(lin . silu(vec)) for each of n_seg vectors
+ * ([issue] "Tensor names": *.lin.weight [9216, 3072] = shift, scale, gate;
+ * SiLU on vec as in the final layer's adaLN, a reading of [issue] "Structure").
+ *   vec   : device [n_seg][3072] fp32
+ *   w_lin : host array of n_seg device pointers, each [9216][3072] bf16
+ *   mod   : device output [n_seg][3][3072] fp32 (shift, scale, gate)
+ */
+int flux3_modulate(const float* vec, const uint16_t* const* w_lin, int n_seg, float* mod,
+                   hipStream_t stream);
+
+/* ---- a3: LayerNorm + modulation --------------------------------------------
+ * out = (1 + scale[m]) * LN(x) + shift[m], LN without affine, eps 1e-6, where
+ * m is the segment of the row ([blog] "Inside one block"; [issue] "Structure").
+ *   x, out  : device [n][3072] bf16 (row strides ldx, ldo)
+ *   seg_off : host [n_seg+1] int, 0 = seg_off[0] < ... < seg_off[n_seg] = n
+ *   mod     : device, segment s uses shift = mod + s*mod_stride and
+ *             scale = shift + 3072 (fp32); mod_stride >= 6144
+ */
+int flux3_ln_modulate(const uint16_t* x, int ldx, uint16_t* out, int ldo, int n,
+                      const int* seg_off, int n_seg, const float* mod, int mod_stride,
+                      hipStream_t stream);
+
+/* ---- a6: QK RMSNorm + RoPE ---------------------------------------------------
+ * In place on q and k of every head ([issue] "Structure"):
+ *   q <- rope(q / sqrt(mean_128(q^2) + 1e-6) * q_scale), same for k.
+ *   q, k    : device [n][24][128] bf16 with row strides ldq, ldk (elements)
+ *   q_scale, k_scale : device [128] bf16 (norm.query_norm / key_norm scale)
+ *   table   : device rope table from flux3_rope_table, [n][64][2] fp32
+ */
+int flux3_qk_norm_rope(uint16_t* q, int ldq, uint16_t* k, int ldk, int n, const uint16_t* q_scale,
+                       const uint16_t* k_scale, const float* table, hipStream_t stream);
+
+/* ---- a7: attention -------------------------------------------------------------
+ * o = softmax(q k^T / sqrt(128)) v per head over all n keys, no mask
+ * ([blog] "Two stages": in the joint blocks every token attends to every
+ * token; stage-1 calls pass one stream's rows only).
+ *   q, k, v : device [n][24][128] bf16, row strides ldq, ldk, ldv
+ *   o       : device output [n][24][128] bf16, row stride ldo
+ * fp32 accumulation; probabilities are rounded to bf16 for the P.V product.
+ */
+int flux3_attention(const uint16_t* q, int ldq, const uint16_t* k, int ldk, const uint16_t* v,
+                    int ldv, uint16_t* o, int ldo, int n, hipStream_t stream);
+
+/* ---- projections -------------------------------------------------------------
+ * flux3_linear: Y = X W^T, fp32 accumulation, rounded to bf16 (or fp32 when
+ * y_f32 is set, then y is ignored).
+ *   x : device [m][k] bf16 (row stride ldx), w : device [n][k] bf16 (stride ldw)
+ *   y : device [m][n] bf16 (stride ldy) or y_f32 : device [m][n] fp32
+ * Requires k % 64 == 0 and n % 64 == 0 (every projection of the model does).
+ */
+int flux3_linear(const uint16_t* x, int ldx, const uint16_t* w, int ldw, uint16_t* y, int ldy,
+                 float* y_f32, int m, int n, int k, hipStream_t stream);
+
+/* ---- packed block weights ------------------------------------------------------
+ * One block's weights in the layout the block kernels read (made once by
+ * flux3_pack_block from the checkpoint tensors):
+ *   w_in  [27648][3072]: rows 0..9215 = q_proj | k_proj | v_proj, rows
+ *         9216.. = mlp_in with its two halves interleaved in groups of 32
+ *         rows (a0..a31, b0..b31, a32..a63, b32..b63, ...), so the SwiGLU
+ *         partner columns of one output tile are computed together;
+ *   w_out [3072][12288]: [attn_out | mlp_out] concatenated along the input
+ *         dimension, so attn_out(o) + mlp_out(h) is one product with [o | h].
+ */
+typedef struct flux3_block_weights {
+  const uint16_t* w_in;     /* device [27648][3072] bf16 */
+  const uint16_t* w_out;    /* device [3072][12288] bf16 */
+  const uint16_t* q_scale;  /* device [128] bf16 */
+  const uint16_t* k_scale;  /* device [128] bf16 */
+} flux3_block_weights;
+
+#define FLUX3_W_IN_ROWS 27648
+#define FLUX3_W_OUT_COLS 12288
+
+/* flux3_pack_block: build w_in and w_out (device outputs, caller-allocated)
+ * from the checkpoint's q_proj, k_proj, v_proj, attn_out [3072][3072],
+ * mlp_in [18432][3072] and mlp_out [3072][9216] (all device bf16). */
+int flux3_pack_block(const uint16_t* q_proj, const uint16_t* k_proj, const uint16_t* v_proj,
+                     const uint16_t* attn_out, const uint16_t* mlp_in, const uint16_t* mlp_out,
+                     uint16_t* w_in, uint16_t* w_out, hipStream_t stream);
+
+/* ---- a3..a8: one block -----------------------------------------------------------
+ * x <- x + gate * (attn_out(attention(rope(rms(q)), rope(rms(k)), v)) +
+ *                  mlp_out(silu(a) * b)),  with q, k, v, [a|b] projections of
+ * h = (1 + scale) LN(x) + shift ([blog] "Inside one block"; [issue] "Structure").
+ *   x        : device [n][3072] bf16, updated in place
+ *   seg_off  : host [n_seg+1] row offsets; segment s uses mod + s*9216
+ *              (shift, scale, gate) fp32 (device)
+ *   table    : device rope table of these n rows
+ *   workspace: device, >= flux3_block_workspace_size(n) bytes
+ * Attention covers all n rows: a stage-1 call passes one stream's rows.
+ */
+size_t flux3_block_workspace_size(int n);
+int flux3_block_forward(uint16_t* x, int n, const int* seg_off, int n_seg, const float* mod,
+                        const flux3_block_weights* w, const float* table, void* workspace,
+                        size_t ws_bytes, hipStream_t stream);
+
+/* ---- conditioning ------------------------------------------------------------------
+ * flux3_time_vectors: per-mode conditioning vectors ([blog] "Every token gets
+ * its own timestep"; [issue] "Structure"):
+ *   vec[image] = time_in(emb(sigma)), vec[other modes] = time_in(emb(0)),
+ *   plus ref_time_in(emb(sigma_next)) on every mode when ref_time_in is given
+ *   (the flow-map checkpoint).  emb(t) = [cos, sin](1000 t f_j),
+ *   f_j = 10000^(-j/128), j < 128; time_in = Linear, SiLU, Linear (no bias).
+ *   w_time   : device {in [3072][256], out [3072][3072]} bf16
+ *   w_ref    : same for ref_time_in, or NULLs for the base checkpoint
+ *   mode_is_image : host [n_modes] (1 for the image mode)
+ *   vec      : device output [n_modes][3072] fp32
+ */
+int flux3_time_vectors(const uint16_t* w_time_in, const uint16_t* w_time_out,
+                       const uint16_t* w_ref_in, const uint16_t* w_ref_out, float sigma,
+                       float sigma_next, const int* mode_is_image, int n_modes, float* vec,
+                       void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---- a9..a12: the whole transformer ---------------------------------------------- */
+typedef struct flux3_model_weights {
+  const uint16_t* emb_in_image;       /* [3072][128] */
+  const uint16_t* emb_in_image_cond;  /* [3072][128] */
+  const uint16_t* txt_in;             /* [3072][20480] */
+  const uint16_t* time_in_w1;         /* [3072][256] */
+  const uint16_t* time_in_w2;         /* [3072][3072] */
+  const uint16_t* ref_time_in_w1;     /* [3072][256], NULL for the base checkpoint */
+  const uint16_t* ref_time_in_w2;     /* [3072][3072], NULL for the base checkpoint */
+  const uint16_t* early_mod[3];       /* image, image_cond, txt: [9216][3072] */
+  const uint16_t* single_mod[3];      /* image, image_cond, txt: [9216][3072] */
+  const flux3_block_weights* early[3];/* host arrays of n_early packed blocks per mode */
+  const flux3_block_weights* single;  /* host array of n_single packed blocks */
+  int n_early;                        /* 5 in the checkpoint */
+  int n_single;                       /* 28 in the checkpoint */
+  const uint16_t* final_ada;          /* [6144][3072] adaLN_modulation.1 */
+  const uint16_t* final_linear;       /* [128][3072] */
+} flux3_model_weights;
+
+/* flux3_stack_workspace_size: bytes of workspace for flux3_stack_forward
+ * with these token counts. */
+size_t flux3_stack_workspace_size(int n_img, int n_cond, int n_txt);
+
+/* flux3_stack_forward: velocity of the image tokens ([blog] "Two stages";
+ * [issue] "Structure"):
+ *   embed (emb_in.image, emb_in.image_cond, txt_in) -> stage 1: each stream
+ *   through its own n_early blocks with its early modulation, attending only
+ *   to itself -> streams concatenated (image, image_cond, text) -> stage 2:
+ *   n_single shared blocks, each token modulated by its stream's single
+ *   modulation -> final layer on the image tokens -> v.
+ *   img   : device [n_img][128] bf16 latents
+ *   cond  : device [n_cond][128] bf16 reference latents (NULL if n_cond = 0)
+ *   txt   : device [n_txt][20480] bf16 text features
+ *   table : device rope table [n_img + n_cond + n_txt][64][2] for the ids of
+ *           flux3_build_ids (same token order)
+ *   sigma, sigma_next : the step's noise level and the one it jumps to
+ *   v     : device output [n_img][128] fp32
+ */
+int flux3_stack_forward(const flux3_model_weights* w, const uint16_t* img, int n_img,
+                        const uint16_t* cond, int n_cond, const uint16_t* txt, int n_txt,
+                        const float* table, float sigma, float sigma_next, float* v,
+                        void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---- a13: sampler update ------------------------------------------------------------
+ * x <- x + (sigma_next - sigma) v, and x_bf16 <- bf16(x) for the next call
+ * ([issue] "Sampling").  x, v: device [n] fp32; x_bf16: device [n] bf16.
+ */
+int flux3_euler_step(float* x, uint16_t* x_bf16, const float* v, int n, float sigma,
+                     float sigma_next, hipStream_t stream);
+
+/* flux3_sigmas: the shifted schedule, host only ([issue] "Sampling"):
+ * t_k = 1 - k/steps, sigma_k = alpha t_k / (1 + (alpha - 1) t_k), k = 0..steps.
+ *   out: host [steps+1] fp32 (computed in fp64). */
+int flux3_sigmas(int steps, double alpha, float* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLUX3_DIT_H */

@@ -1,0 +1,607 @@
+// C ABI of flux3_dit: argument checks, workspace layout and the block / stack
+// drivers.  The declarations and their citations are in include/flux3_dit.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/flux3_dit.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace flux3;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FLUX3_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return FLUX3_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(p) REQUIRE((p) != nullptr && aligned16(p), FLUX3_EINVAL, "%s: null or not 16-byte aligned", #p)
+#define REQUIRE_LD(ld, minv) REQUIRE((ld) >= (minv) && (ld) % 8 == 0, FLUX3_EINVAL, "%s=%d must be >= %d and a multiple of 8", #ld, (int)(ld), (int)(minv))
+
+int make_segs(const int* seg_off, int n_seg, int n, SegTable* out) {
+  REQUIRE(seg_off != nullptr, FLUX3_EINVAL, "seg_off is null");
+  REQUIRE(n_seg >= 1 && n_seg <= kMaxSeg, FLUX3_EINVAL, "n_seg=%d must be in 1..%d", n_seg, kMaxSeg);
+  REQUIRE(seg_off[0] == 0 && seg_off[n_seg] == n, FLUX3_EINVAL,
+          "seg_off must start at 0 and end at n=%d", n);
+  for (int i = 0; i < n_seg; ++i)
+    REQUIRE(seg_off[i] < seg_off[i + 1], FLUX3_EINVAL, "seg_off must be strictly increasing");
+  memset(out, 0, sizeof(*out));
+  for (int i = 0; i <= n_seg; ++i) out->off[i] = seg_off[i];
+  out->n = n_seg;
+  return FLUX3_OK;
+}
+
+const bf16* B(const uint16_t* p) { return reinterpret_cast<const bf16*>(p); }
+bf16* B(uint16_t* p) { return reinterpret_cast<bf16*>(p); }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Block workspace: xm [n][3072] | qkv [n][9216] | cat [n][12288], bf16.
+struct BlockWs {
+  bf16* xm;
+  bf16* qkv;
+  bf16* cat;
+};
+
+size_t block_ws_bytes(int n) {
+  return align256((size_t)n * kHidden * 2) + align256((size_t)n * 3 * kHidden * 2) +
+         align256((size_t)n * kWOutCols * 2);
+}
+
+BlockWs carve_block_ws(void* ws, int n) {
+  char* p = (char*)ws;
+  BlockWs w;
+  w.xm = (bf16*)p;
+  p += align256((size_t)n * kHidden * 2);
+  w.qkv = (bf16*)p;
+  p += align256((size_t)n * 3 * kHidden * 2);
+  w.cat = (bf16*)p;
+  return w;
+}
+
+int check_block_weights(const flux3_block_weights* w) {
+  REQUIRE(w != nullptr, FLUX3_EINVAL, "block weights are null");
+  REQUIRE_PTR(w->w_in);
+  REQUIRE_PTR(w->w_out);
+  REQUIRE_PTR(w->q_scale);
+  REQUIRE_PTR(w->k_scale);
+  return FLUX3_OK;
+}
+
+// a3..a8 with arguments already checked.
+void block_forward_unchecked(bf16* x, int n, const SegTable& seg, const float* mod,
+                             const flux3_block_weights* w, const float* table, const BlockWs& ws,
+                             hipStream_t st) {
+  // a3: h = (1 + scale) LN(x) + shift
+  launch_ln_modulate(x, kHidden, ws.xm, kHidden, n, seg, mod, 3 * kHidden, st);
+  // a4 + a5: [q | k | v] and h_mlp = silu(a) * b in one product over w_in
+  GemmArgs g{};
+  g.A = ws.xm;
+  g.lda = kHidden;
+  g.B = B(w->w_in);
+  g.ldb = kHidden;
+  g.M = n;
+  g.N = kWInRows;
+  g.K = kHidden;
+  g.epi = GemmEpi::kInProj;
+  g.C = ws.qkv;
+  g.ldc = 3 * kHidden;
+  g.H = ws.cat + kHidden;
+  g.ldh = kWOutCols;
+  launch_gemm(g, st);
+  // a6: RMSNorm + RoPE on q and k
+  launch_qk_norm_rope(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, n, B(w->q_scale),
+                      B(w->k_scale), table, st);
+  // a7: attention -> first 3072 columns of cat
+  launch_attention(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, ws.qkv + 2 * kHidden,
+                   3 * kHidden, ws.cat, kWOutCols, n, st);
+  // a8: x += gate * ([o | h] [W_o | W_out]^T)
+  GemmArgs o{};
+  o.A = ws.cat;
+  o.lda = kWOutCols;
+  o.B = B(w->w_out);
+  o.ldb = kWOutCols;
+  o.M = n;
+  o.N = kHidden;
+  o.K = kWOutCols;
+  o.epi = GemmEpi::kGatedResidual;
+  o.C = x;
+  o.ldc = kHidden;
+  o.mod = mod;
+  o.mod_stride = 3 * kHidden;
+  o.gate_offset = 2 * kHidden;
+  o.seg = seg;
+  launch_gemm(o, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flux3_last_error(void) { return g_err; }
+
+int flux3_version(void) { return 100; }
+
+int flux3_build_ids(int img_h, int img_w, int n_refs, const int* ref_hw, int n_txt, float* ids,
+                    int* n_out) {
+  REQUIRE(img_h >= 0 && img_w >= 0 && n_txt >= 0 && n_refs >= 0, FLUX3_EINVAL,
+          "sizes must be non-negative");
+  REQUIRE(n_refs == 0 || ref_hw != nullptr, FLUX3_EINVAL, "ref_hw is null");
+  REQUIRE(n_out != nullptr, FLUX3_EINVAL, "n_out is null");
+  long n = (long)img_h * img_w + n_txt;
+  for (int k = 0; k < n_refs; ++k) {
+    REQUIRE(ref_hw[2 * k] >= 0 && ref_hw[2 * k + 1] >= 0, FLUX3_EINVAL, "bad reference grid");
+    n += (long)ref_hw[2 * k] * ref_hw[2 * k + 1];
+  }
+  REQUIRE(n < (1L << 30), FLUX3_EINVAL, "too many tokens");
+  *n_out = (int)n;
+  if (!ids) return FLUX3_OK;
+  float* p = ids;
+  for (int r = 0; r < img_h; ++r)
+    for (int c = 0; c < img_w; ++c) {
+      p[0] = 0.f; p[1] = 0.5f * r; p[2] = 0.5f * c; p[3] = 0.f;
+      p += 4;
+    }
+  for (int k = 0; k < n_refs; ++k)
+    for (int r = 0; r < ref_hw[2 * k]; ++r)
+      for (int c = 0; c < ref_hw[2 * k + 1]; ++c) {
+        p[0] = 0.f; p[1] = 0.5f * r; p[2] = 0.5f * c; p[3] = -(float)(k + 1);
+        p += 4;
+      }
+  for (int i = 0; i < n_txt; ++i) {
+    p[0] = 0.f; p[1] = 0.f; p[2] = 0.f; p[3] = (float)i;
+    p += 4;
+  }
+  return FLUX3_OK;
+}
+
+int flux3_rope_table(const float* ids, int n, float* table, hipStream_t stream) {
+  REQUIRE(n >= 0, FLUX3_EINVAL, "n=%d", n);
+  if (n == 0) return FLUX3_OK;
+  REQUIRE_PTR(ids);
+  REQUIRE_PTR(table);
+  launch_rope_table(ids, n, table, stream);
+  return check_launch("rope_table");
+}
+
+int flux3_modulate(const float* vec, const uint16_t* const* w_lin, int n_seg, float* mod,
+                   hipStream_t stream) {
+  REQUIRE(n_seg >= 1 && n_seg <= kMaxSeg, FLUX3_EINVAL, "n_seg=%d must be in 1..%d", n_seg, kMaxSeg);
+  REQUIRE_PTR(vec);
+  REQUIRE_PTR(mod);
+  REQUIRE(w_lin != nullptr, FLUX3_EINVAL, "w_lin is null");
+  GemvBatch b{};
+  for (int s = 0; s < n_seg; ++s) {
+    REQUIRE(w_lin[s] != nullptr && aligned16(w_lin[s]), FLUX3_EINVAL, "w_lin[%d] null or misaligned", s);
+    b.w[s] = B(w_lin[s]);
+    b.x[s] = vec + (size_t)s * kHidden;
+    b.y[s] = mod + (size_t)s * 3 * kHidden;
+  }
+  launch_gemv(b, n_seg, 3 * kHidden, kHidden, true, false, stream);
+  return check_launch("modulate");
+}
+
+int flux3_ln_modulate(const uint16_t* x, int ldx, uint16_t* out, int ldo, int n,
+                      const int* seg_off, int n_seg, const float* mod, int mod_stride,
+                      hipStream_t stream) {
+  REQUIRE(n >= 0, FLUX3_EINVAL, "n=%d", n);
+  if (n == 0) return FLUX3_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(out);
+  REQUIRE_PTR(mod);
+  REQUIRE_LD(ldx, kHidden);
+  REQUIRE_LD(ldo, kHidden);
+  REQUIRE(mod_stride >= 2 * kHidden && mod_stride % 4 == 0, FLUX3_EINVAL, "mod_stride=%d", mod_stride);
+  SegTable seg;
+  int rc = make_segs(seg_off, n_seg, n, &seg);
+  if (rc) return rc;
+  launch_ln_modulate(B(x), ldx, B(out), ldo, n, seg, mod, mod_stride, stream);
+  return check_launch("ln_modulate");
+}
+
+int flux3_qk_norm_rope(uint16_t* q, int ldq, uint16_t* k, int ldk, int n, const uint16_t* q_scale,
+                       const uint16_t* k_scale, const float* table, hipStream_t stream) {
+  REQUIRE(n >= 0, FLUX3_EINVAL, "n=%d", n);
+  if (n == 0) return FLUX3_OK;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(q_scale);
+  REQUIRE_PTR(k_scale);
+  REQUIRE_PTR(table);
+  REQUIRE_LD(ldq, kHidden);
+  REQUIRE_LD(ldk, kHidden);
+  launch_qk_norm_rope(B(q), ldq, B(k), ldk, n, B(q_scale), B(k_scale), table, stream);
+  return check_launch("qk_norm_rope");
+}
+
+int flux3_attention(const uint16_t* q, int ldq, const uint16_t* k, int ldk, const uint16_t* v,
+                    int ldv, uint16_t* o, int ldo, int n, hipStream_t stream) {
+  REQUIRE(n >= 0, FLUX3_EINVAL, "n=%d", n);
+  if (n == 0) return FLUX3_OK;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(o);
+  REQUIRE_LD(ldq, kHidden);
+  REQUIRE_LD(ldk, kHidden);
+  REQUIRE_LD(ldv, kHidden);
+  REQUIRE_LD(ldo, kHidden);
+  launch_attention(B(q), ldq, B(k), ldk, B(v), ldv, B(o), ldo, n, stream);
+  return check_launch("attention");
+}
+
+int flux3_linear(const uint16_t* x, int ldx, const uint16_t* w, int ldw, uint16_t* y, int ldy,
+                 float* y_f32, int m, int n, int k, hipStream_t stream) {
+  REQUIRE(m >= 0 && n > 0 && k > 0, FLUX3_EINVAL, "m=%d n=%d k=%d", m, n, k);
+  REQUIRE(k % 64 == 0 && n % 64 == 0, FLUX3_EUNSUPPORTED, "k=%d and n=%d must be multiples of 64", k, n);
+  if (m == 0) return FLUX3_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w);
+  REQUIRE_LD(ldx, k);
+  REQUIRE_LD(ldw, k);
+  GemmArgs g{};
+  g.A = B(x);
+  g.lda = ldx;
+  g.B = B(w);
+  g.ldb = ldw;
+  g.M = m;
+  g.N = n;
+  g.K = k;
+  if (y_f32) {
+    REQUIRE_PTR(y_f32);
+    REQUIRE(ldy >= n && ldy % 4 == 0, FLUX3_EINVAL, "ldy=%d", ldy);
+    g.epi = GemmEpi::kStoreF32;
+    g.C = y_f32;
+  } else {
+    REQUIRE_PTR(y);
+    REQUIRE_LD(ldy, n);
+    g.epi = GemmEpi::kStoreBf16;
+    g.C = y;
+  }
+  g.ldc = ldy;
+  launch_gemm(g, stream);
+  return check_launch("linear");
+}
+
+int flux3_pack_block(const uint16_t* q_proj, const uint16_t* k_proj, const uint16_t* v_proj,
+                     const uint16_t* attn_out, const uint16_t* mlp_in, const uint16_t* mlp_out,
+                     uint16_t* w_in, uint16_t* w_out, hipStream_t stream) {
+  REQUIRE_PTR(q_proj);
+  REQUIRE_PTR(k_proj);
+  REQUIRE_PTR(v_proj);
+  REQUIRE_PTR(attn_out);
+  REQUIRE_PTR(mlp_in);
+  REQUIRE_PTR(mlp_out);
+  REQUIRE_PTR(w_in);
+  REQUIRE_PTR(w_out);
+  launch_pack_block(B(q_proj), B(k_proj), B(v_proj), B(attn_out), B(mlp_in), B(mlp_out), B(w_in),
+                    B(w_out), stream);
+  return check_launch("pack_block");
+}
+
+size_t flux3_block_workspace_size(int n) { return n > 0 ? block_ws_bytes(n) : 0; }
+
+int flux3_block_forward(uint16_t* x, int n, const int* seg_off, int n_seg, const float* mod,
+                        const flux3_block_weights* w, const float* table, void* workspace,
+                        size_t ws_bytes, hipStream_t stream) {
+  REQUIRE(n >= 0, FLUX3_EINVAL, "n=%d", n);
+  if (n == 0) return FLUX3_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(mod);
+  REQUIRE_PTR(table);
+  int rc = check_block_weights(w);
+  if (rc) return rc;
+  SegTable seg;
+  rc = make_segs(seg_off, n_seg, n, &seg);
+  if (rc) return rc;
+  REQUIRE(workspace != nullptr && aligned16(workspace), FLUX3_EWORKSPACE, "workspace missing or misaligned");
+  REQUIRE(ws_bytes >= block_ws_bytes(n), FLUX3_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes,
+          block_ws_bytes(n));
+  block_forward_unchecked(B(x), n, seg, mod, w, table, carve_block_ws(workspace, n), stream);
+  return check_launch("block_forward");
+}
+
+// ---- conditioning and the whole stack -----------------------------------------------
+
+namespace {
+// Scratch of flux3_time_vectors: emb [3][256] | hidden [2][8][3072] (fp32).
+constexpr size_t kTimeWsBytes = 3 * 256 * 4 + 2 * kMaxSeg * kHidden * 4;
+
+// vec[m] = time_in(emb(t_m)) (+ ref_time_in(emb(sigma_next))), t_m = sigma for
+// image, 0 otherwise.  Embeddings: index 0 = emb(sigma), 1 = emb(0),
+// 2 = emb(sigma_next).
+int time_vectors_unchecked(const uint16_t* w1, const uint16_t* w2, const uint16_t* r1,
+                           const uint16_t* r2, float sigma, float sigma_next,
+                           const int* is_image, int n_modes, float* vec, char* ws,
+                           hipStream_t st) {
+  float* emb = (float*)ws;
+  float* hid = emb + 3 * 256;
+  const Timesteps ts{{sigma, 0.f, sigma_next, 0.f}};
+  launch_timestep_embedding(ts, 3, emb, st);
+  GemvBatch b{};
+  for (int m = 0; m < n_modes; ++m) {
+    b.w[m] = B(w1);
+    b.x[m] = emb + (is_image[m] ? 0 : 256);
+    b.y[m] = hid + (size_t)m * kHidden;
+  }
+  launch_gemv(b, n_modes, kHidden, 256, false, false, st);
+  for (int m = 0; m < n_modes; ++m) {
+    b.w[m] = B(w2);
+    b.x[m] = hid + (size_t)m * kHidden;
+    b.y[m] = vec + (size_t)m * kHidden;
+  }
+  launch_gemv(b, n_modes, kHidden, kHidden, true, false, st);
+  if (r1 && r2) {
+    float* rh = hid + (size_t)kMaxSeg * kHidden;
+    GemvBatch r{};
+    r.w[0] = B(r1);
+    r.x[0] = emb + 512;
+    r.y[0] = rh;
+    launch_gemv(r, 1, kHidden, 256, false, false, st);
+    for (int m = 0; m < n_modes; ++m) {
+      b.w[m] = B(r2);
+      b.x[m] = rh;
+      b.y[m] = vec + (size_t)m * kHidden;
+    }
+    launch_gemv(b, n_modes, kHidden, kHidden, true, true, st);
+  }
+  return check_launch("time_vectors");
+}
+
+// Stack workspace layout.
+struct StackWs {
+  bf16* x;          // [N][3072] residual stream, tokens image | image_cond | txt
+  float* vec;       // [3][3072]
+  float* mod_early; // [3][9216]
+  float* mod_single;// [3][9216]
+  float* mod_final; // [6144]
+  char* time_ws;    // kTimeWsBytes
+  void* block_ws;   // block workspace for N rows
+  size_t block_ws_bytes;
+};
+
+size_t stack_ws_bytes(int n_total) {
+  return align256((size_t)n_total * kHidden * 2) + align256(3 * kHidden * 4) +
+         2 * align256(3 * 3 * kHidden * 4) + align256(2 * kHidden * 4) + align256(kTimeWsBytes) +
+         block_ws_bytes(n_total);
+}
+
+StackWs carve_stack_ws(void* ws, int n_total) {
+  char* p = (char*)ws;
+  StackWs s;
+  s.x = (bf16*)p;
+  p += align256((size_t)n_total * kHidden * 2);
+  s.vec = (float*)p;
+  p += align256(3 * kHidden * 4);
+  s.mod_early = (float*)p;
+  p += align256(3 * 3 * kHidden * 4);
+  s.mod_single = (float*)p;
+  p += align256(3 * 3 * kHidden * 4);
+  s.mod_final = (float*)p;
+  p += align256(2 * kHidden * 4);
+  s.time_ws = p;
+  p += align256(kTimeWsBytes);
+  s.block_ws = p;
+  s.block_ws_bytes = block_ws_bytes(n_total);
+  return s;
+}
+}  // namespace
+
+int flux3_time_vectors(const uint16_t* w_time_in, const uint16_t* w_time_out,
+                       const uint16_t* w_ref_in, const uint16_t* w_ref_out, float sigma,
+                       float sigma_next, const int* mode_is_image, int n_modes, float* vec,
+                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+  REQUIRE_PTR(w_time_in);
+  REQUIRE_PTR(w_time_out);
+  REQUIRE((w_ref_in == nullptr) == (w_ref_out == nullptr), FLUX3_EINVAL,
+          "ref_time_in weights: give both or neither");
+  if (w_ref_in) {
+    REQUIRE_PTR(w_ref_in);
+    REQUIRE_PTR(w_ref_out);
+  }
+  REQUIRE(n_modes >= 1 && n_modes <= kMaxSeg, FLUX3_EINVAL, "n_modes=%d", n_modes);
+  REQUIRE(mode_is_image != nullptr, FLUX3_EINVAL, "mode_is_image is null");
+  REQUIRE_PTR(vec);
+  REQUIRE(workspace != nullptr && aligned16(workspace) && ws_bytes >= kTimeWsBytes,
+          FLUX3_EWORKSPACE, "time_vectors needs %zu bytes of workspace", kTimeWsBytes);
+  return time_vectors_unchecked(w_time_in, w_time_out, w_ref_in, w_ref_out, sigma, sigma_next,
+                                mode_is_image, n_modes, vec, (char*)workspace, stream);
+}
+
+size_t flux3_stack_workspace_size(int n_img, int n_cond, int n_txt) {
+  const long n = (long)n_img + n_cond + n_txt;
+  if (n_img <= 0 || n_cond < 0 || n_txt < 0 || n >= (1L << 30)) return 0;
+  return stack_ws_bytes((int)n);
+}
+
+int flux3_stack_forward(const flux3_model_weights* w, const uint16_t* img, int n_img,
+                        const uint16_t* cond, int n_cond, const uint16_t* txt, int n_txt,
+                        const float* table, float sigma, float sigma_next, float* v,
+                        void* workspace, size_t ws_bytes, hipStream_t stream) {
+  REQUIRE(w != nullptr, FLUX3_EINVAL, "weights are null");
+  REQUIRE(n_img > 0 && n_cond >= 0 && n_txt >= 0, FLUX3_EINVAL, "n_img=%d n_cond=%d n_txt=%d",
+          n_img, n_cond, n_txt);
+  REQUIRE_PTR(img);
+  REQUIRE(n_cond == 0 || (cond != nullptr && aligned16(cond)), FLUX3_EINVAL, "cond null or misaligned");
+  REQUIRE(n_txt == 0 || (txt != nullptr && aligned16(txt)), FLUX3_EINVAL, "txt null or misaligned");
+  REQUIRE_PTR(table);
+  REQUIRE_PTR(v);
+  REQUIRE(w->n_early >= 0 && w->n_single >= 0, FLUX3_EINVAL, "block counts");
+  REQUIRE_PTR(w->emb_in_image);
+  REQUIRE(n_cond == 0 || (w->emb_in_image_cond && aligned16(w->emb_in_image_cond)), FLUX3_EINVAL,
+          "emb_in_image_cond missing");
+  REQUIRE(n_txt == 0 || (w->txt_in && aligned16(w->txt_in)), FLUX3_EINVAL, "txt_in missing");
+  REQUIRE_PTR(w->time_in_w1);
+  REQUIRE_PTR(w->time_in_w2);
+  REQUIRE((w->ref_time_in_w1 == nullptr) == (w->ref_time_in_w2 == nullptr), FLUX3_EINVAL,
+          "ref_time_in weights: give both or neither");
+  REQUIRE_PTR(w->final_ada);
+  REQUIRE_PTR(w->final_linear);
+  const int n_total = n_img + n_cond + n_txt;
+  REQUIRE(workspace != nullptr && aligned16(workspace), FLUX3_EWORKSPACE, "workspace missing");
+  REQUIRE(ws_bytes >= stack_ws_bytes(n_total), FLUX3_EWORKSPACE, "workspace %zu < %zu bytes",
+          ws_bytes, stack_ws_bytes(n_total));
+
+  // Streams present, in token order.
+  int modes[3], counts[3], n_modes = 0;
+  const int all_counts[3] = {n_img, n_cond, n_txt};
+  for (int m = 0; m < 3; ++m)
+    if (all_counts[m] > 0) {
+      modes[n_modes] = m;
+      counts[n_modes] = all_counts[m];
+      ++n_modes;
+    }
+  for (int i = 0; i < n_modes; ++i) {
+    const int m = modes[i];
+    REQUIRE(w->early_mod[m] && aligned16(w->early_mod[m]), FLUX3_EINVAL, "early_mod[%d] missing", m);
+    REQUIRE(w->single_mod[m] && aligned16(w->single_mod[m]), FLUX3_EINVAL, "single_mod[%d] missing", m);
+    REQUIRE(w->n_early == 0 || w->early[m] != nullptr, FLUX3_EINVAL, "early[%d] missing", m);
+    for (int b = 0; b < w->n_early; ++b) {
+      int rc = check_block_weights(&w->early[m][b]);
+      if (rc) return rc;
+    }
+  }
+  REQUIRE(w->n_single == 0 || w->single != nullptr, FLUX3_EINVAL, "single blocks missing");
+  for (int b = 0; b < w->n_single; ++b) {
+    int rc = check_block_weights(&w->single[b]);
+    if (rc) return rc;
+  }
+
+  StackWs s = carve_stack_ws(workspace, n_total);
+  const BlockWs bws = carve_block_ws(s.block_ws, n_total);
+
+  // a13 / conditioning: per-mode vectors, then the 2 x n_modes modulations and
+  // the final adaLN (SiLU then Linear).
+  int is_image[3];
+  for (int i = 0; i < n_modes; ++i) is_image[i] = modes[i] == 0;
+  int rc = time_vectors_unchecked(w->time_in_w1, w->time_in_w2, w->ref_time_in_w1,
+                                  w->ref_time_in_w2, sigma, sigma_next, is_image, n_modes, s.vec,
+                                  s.time_ws, stream);
+  if (rc) return rc;
+  GemvBatch mb{};
+  for (int i = 0; i < n_modes; ++i) {
+    mb.w[i] = B(w->early_mod[modes[i]]);
+    mb.x[i] = s.vec + (size_t)i * kHidden;
+    mb.y[i] = s.mod_early + (size_t)i * 3 * kHidden;
+    mb.w[n_modes + i] = B(w->single_mod[modes[i]]);
+    mb.x[n_modes + i] = s.vec + (size_t)i * kHidden;
+    mb.y[n_modes + i] = s.mod_single + (size_t)i * 3 * kHidden;
+  }
+  launch_gemv(mb, 2 * n_modes, 3 * kHidden, kHidden, true, false, stream);
+  GemvBatch fb{};
+  fb.w[0] = B(w->final_ada);
+  fb.x[0] = s.vec;  // the image mode is always first
+  fb.y[0] = s.mod_final;
+  launch_gemv(fb, 1, 2 * kHidden, kHidden, true, false, stream);
+
+  // a9: embeddings into the residual stream.
+  const uint16_t* inputs[3] = {img, cond, txt};
+  const uint16_t* emb_w[3] = {w->emb_in_image, w->emb_in_image_cond, w->txt_in};
+  const int in_dim[3] = {128, 128, 20480};
+  int row0[3];
+  {
+    int r = 0;
+    for (int i = 0; i < n_modes; ++i) {
+      row0[i] = r;
+      r += counts[i];
+    }
+  }
+  for (int i = 0; i < n_modes; ++i) {
+    const int m = modes[i];
+    GemmArgs g{};
+    g.A = B(inputs[m]);
+    g.lda = in_dim[m];
+    g.B = B(emb_w[m]);
+    g.ldb = in_dim[m];
+    g.M = counts[i];
+    g.N = kHidden;
+    g.K = in_dim[m];
+    g.epi = GemmEpi::kStoreBf16;
+    g.C = s.x + (size_t)row0[i] * kHidden;
+    g.ldc = kHidden;
+    launch_gemm(g, stream);
+  }
+
+  // a10: stage 1, each stream on its own rows with its own blocks.
+  for (int i = 0; i < n_modes; ++i) {
+    const int m = modes[i];
+    SegTable seg{};
+    seg.off[0] = 0;
+    seg.off[1] = counts[i];
+    seg.n = 1;
+    for (int b = 0; b < w->n_early; ++b)
+      block_forward_unchecked(s.x + (size_t)row0[i] * kHidden, counts[i], seg,
+                              s.mod_early + (size_t)i * 3 * kHidden, &w->early[m][b],
+                              table + (size_t)row0[i] * 128, bws, stream);
+  }
+
+  // a11: stage 2, all tokens, per-row modulation by stream.
+  SegTable seg{};
+  for (int i = 0; i < n_modes; ++i) seg.off[i] = row0[i];
+  seg.off[n_modes] = n_total;
+  seg.n = n_modes;
+  for (int b = 0; b < w->n_single; ++b)
+    block_forward_unchecked(s.x, n_total, seg, s.mod_single, &w->single[b], table, bws, stream);
+
+  // a12: final layer on the image rows.
+  SegTable one{};
+  one.off[1] = n_img;
+  one.n = 1;
+  launch_ln_modulate(s.x, kHidden, bws.xm, kHidden, n_img, one, s.mod_final, 2 * kHidden, stream);
+  GemmArgs f{};
+  f.A = bws.xm;
+  f.lda = kHidden;
+  f.B = B(w->final_linear);
+  f.ldb = kHidden;
+  f.M = n_img;
+  f.N = 128;
+  f.K = kHidden;
+  f.epi = GemmEpi::kStoreF32;
+  f.C = v;
+  f.ldc = 128;
+  launch_gemm(f, stream);
+  return check_launch("stack_forward");
+}
+
+int flux3_euler_step(float* x, uint16_t* x_bf16, const float* v, int n, float sigma,
+                     float sigma_next, hipStream_t stream) {
+  REQUIRE(n >= 0, FLUX3_EINVAL, "n=%d", n);
+  if (n == 0) return FLUX3_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(v);
+  REQUIRE(x_bf16 == nullptr || aligned16(x_bf16), FLUX3_EINVAL, "x_bf16 misaligned");
+  launch_euler(x, B(x_bf16), v, n, sigma_next - sigma, stream);
+  return check_launch("euler_step");
+}
+
+int flux3_sigmas(int steps, double alpha, float* out) {
+  REQUIRE(steps >= 1 && out != nullptr && alpha > 0, FLUX3_EINVAL, "steps=%d alpha=%g", steps, alpha);
+  for (int k = 0; k <= steps; ++k) {
+    const double t = 1.0 - (double)k / steps;
+    out[k] = (float)(alpha * t / (1.0 + (alpha - 1.0) * t));
+  }
+  return FLUX3_OK;
+}
+
+}  // extern "C"

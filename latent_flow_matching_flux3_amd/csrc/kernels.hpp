@@ -1,0 +1,61 @@
+// Internal launch interface between the C ABI and the kernels.
+#pragma once
+
+#include "common.hpp"
+
+namespace flux3 {
+
+struct GemvBatch {
+  const bf16* w[kMaxSeg];
+  const float* x[kMaxSeg];
+  float* y[kMaxSeg];
+};
+
+// Epilogue selector of the bf16 MFMA GEMM  C = A B^T  (A [M][K], B [N][K]).
+enum class GemmEpi {
+  kStoreBf16,     // C bf16 [M][N], stride ldc
+  kStoreF32,      // C fp32 [M][N], stride ldc
+  kInProj,        // cols < 9216: q|k|v store; cols >= 9216: SwiGLU of interleaved a/b -> h
+  kGatedResidual  // x[row][col] += gate[seg(row)][col] * acc
+};
+
+struct GemmArgs {
+  const bf16* A;
+  int lda;
+  const bf16* B;
+  int ldb;
+  int M, N, K;
+  GemmEpi epi;
+  // kStoreBf16 / kStoreF32 / kInProj(q|k|v part) / kGatedResidual (x)
+  void* C;
+  int ldc;
+  // kInProj: h output (bf16, stride ldh)
+  bf16* H;
+  int ldh;
+  // kGatedResidual: gate of segment s at mod + s * mod_stride + gate_offset
+  const float* mod;
+  int mod_stride;
+  int gate_offset;
+  SegTable seg;
+};
+
+void launch_ln_modulate(const bf16* x, int ldx, bf16* out, int ldo, int n, const SegTable& seg,
+                        const float* mod, int mod_stride, hipStream_t st);
+void launch_rope_table(const float* ids, int n, float* table, hipStream_t st);
+void launch_qk_norm_rope(bf16* q, int ldq, bf16* k, int ldk, int n, const bf16* q_scale,
+                         const bf16* k_scale, const float* table, hipStream_t st);
+void launch_attention(const bf16* q, int ldq, const bf16* k, int ldk, const bf16* v, int ldv,
+                      bf16* o, int ldo, int n, hipStream_t st);
+void launch_gemm(const GemmArgs& a, hipStream_t st);
+struct Timesteps {
+  float t[4];
+};
+void launch_timestep_embedding(const Timesteps& ts, int nt, float* out, hipStream_t st);
+void launch_gemv(const GemvBatch& batch, int nb, int rows, int K, bool silu_x, bool accumulate,
+                 hipStream_t st);
+void launch_euler(float* x, bf16* xb, const float* v, int n, float dt, hipStream_t st);
+void launch_pack_block(const bf16* wq, const bf16* wk, const bf16* wv, const bf16* wo,
+                       const bf16* w_mlp_in, const bf16* w_mlp_out, bf16* w_in, bf16* w_out,
+                       hipStream_t st);
+
+}  // namespace flux3

@@ -1,0 +1,88 @@
+"""The C ABI: the library loads and exports every function include/flux3_dit.h
+declares; host-side argument checks return status codes (no GPU needed: no
+case below reaches a HIP call)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flux3_dit.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flux3_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import latent_flow_matching_flux3_amd as L
+    L.lib()
+    return L
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 15
+    raw = C.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert sorted(L.EXPORTS) == names
+
+
+def test_version(L):
+    assert L.flux3_version() >= 100
+
+
+def test_build_ids_matches_oracle(L):
+    for h, w, nt, refs in ((0, 0, 5, []), (3, 4, 0, []), (2, 3, 4, [(1, 2), (3, 1)]), (64, 64, 512, [(64, 64)])):
+        ids = L.flux3_build_ids(h, w, nt, refs).numpy().astype(np.float64)
+        np.testing.assert_array_equal(ids, O.build_ids(h, w, nt, refs))
+
+
+def test_sigmas_match_oracle(L):
+    for steps in (1, 16, 50):
+        np.testing.assert_allclose(L.flux3_sigmas(steps).numpy(), O.sigmas(steps), rtol=1e-7, atol=1e-7)
+
+
+def test_error_codes(L):
+    lib = L.lib()
+    n = C.c_int(0)
+    assert lib.flux3_build_ids(-1, 2, 0, None, 0, None, C.byref(n)) == L.EINVAL
+    assert b"non-negative" in lib.flux3_last_error()
+    assert lib.flux3_build_ids(1, 1, 1, None, 0, None, C.byref(n)) == L.EINVAL
+    # unsupported GEMM shape
+    assert lib.flux3_linear(16, 128, 16, 128, 16, 64, None, 4, 64, 100, None) == L.EUNSUPPORTED
+    # null pointer
+    assert lib.flux3_linear(None, 128, 16, 128, 16, 64, None, 4, 64, 128, None) == L.EINVAL
+    # misaligned pointer
+    assert lib.flux3_linear(18, 128, 16, 128, 16, 64, None, 4, 64, 128, None) == L.EINVAL
+    # bad leading dimension
+    assert lib.flux3_linear(16, 100, 16, 128, 16, 64, None, 4, 64, 128, None) == L.EINVAL
+    # segments that do not cover the rows
+    segs = (C.c_int * 3)(0, 3, 6)
+    assert lib.flux3_ln_modulate(16, 3072, 16, 3072, 7, segs, 2, 16, 9216, None) == L.EINVAL
+    segs = (C.c_int * 3)(0, 3, 3)
+    assert lib.flux3_ln_modulate(16, 3072, 16, 3072, 3, segs, 2, 16, 9216, None) == L.EINVAL
+    # too many segments
+    segs = (C.c_int * 10)(*range(10))
+    assert lib.flux3_ln_modulate(16, 3072, 16, 3072, 9, segs, 9, 16, 9216, None) == L.EINVAL
+    # workspace too small for the block
+    w = L.BlockWeightsC(16, 16, 16, 16)
+    segs = (C.c_int * 2)(0, 10)
+    assert lib.flux3_block_forward(16, 10, segs, 1, 16, C.byref(w), 16, 16, 100, None) == L.EWORKSPACE
+    assert lib.flux3_block_forward(16, 10, segs, 1, 16, C.byref(w), 16, None, 1 << 30, None) == L.EWORKSPACE
+    # empty inputs are a no-op
+    assert lib.flux3_attention(None, 3072, None, 3072, None, 3072, None, 3072, 0, None) == L.OK
+    assert lib.flux3_block_forward(None, 0, None, 0, None, None, None, None, 0, None) == L.OK
+    # workspace sizes grow with n and are 0 for n = 0
+    assert L.flux3_block_workspace_size(0) == 0
+    assert L.flux3_block_workspace_size(4608) >= 4608 * (3072 + 9216 + 12288) * 2
+    assert L.flux3_stack_workspace_size(4096, 0, 512) > L.flux3_block_workspace_size(4608)
+    assert L.flux3_stack_workspace_size(0, 0, 512) == 0

@@ -1,0 +1,254 @@
+"""GPU parity of each entry point against the CPU oracle, at sizes the oracle
+finishes in seconds that still span several tiles and a ragged tail.
+
+Inputs come from flux3_synth (seeded, bf16); both sides read the same values.
+All calls go through the C ABI (latent_flow_matching_flux3_amd)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import flux3_synth as syn
+import oracle as O
+from gpu_util import assert_agree, dev, f64, require_gpu, say, to_f64, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    return require_gpu()
+
+
+# ---- a1: ids and rope table ------------------------------------------------------
+
+@pytest.mark.parametrize("lay", [(8, 8, 32, []), (64, 64, 512, [(64, 64)]), (3, 5, 7, [(2, 2), (4, 1)]),
+                                 (48, 85, 640, [(48, 85)])])
+def test_ids_bit_exact_and_rope_table(L, lay):
+    h, w, nt, refs = lay
+    ids = L.flux3_build_ids(h, w, nt, refs)
+    ref = O.build_ids(h, w, nt, refs)
+    np.testing.assert_array_equal(ids.numpy().astype(np.float64), ref)   # bit-exact
+    say(f"rope_table n={len(ids)}")
+    tab = L.flux3_rope_table(dev(ids))
+    torch.cuda.synchronize()
+    ang = O.rope_angles(ref).reshape(len(ref), 64)
+    expect = np.stack([np.cos(ang), np.sin(ang)], -1).astype(np.float32)
+    got = tab.cpu().numpy()
+    # <= 2 ulp of fp32 (values are in [-1, 1])
+    assert np.max(np.abs(got - expect)) <= 2 * 2.0 ** -24 * 1.0 + 1e-12
+
+
+# ---- GEMMs -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 64), (37, 128, 192), (300, 256, 320), (130, 3072, 128),
+                                   (1030, 13312, 128), (513, 27648, 64), (96, 3072, 12288)])
+def test_linear(L, m, n, k):
+    x = syn.normal_bf16((m, k), 1.0, 11, f"lin.x.{m}.{k}")
+    w = syn.normal_bf16((n, k), 0.02, 12, f"lin.w.{n}.{k}")
+    say(f"linear m={m} n={n} k={k}")
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    L.flux3_linear(dev(x), dev(w), y=y)
+    yf = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    L.flux3_linear(dev(x), dev(w), y_f32=yf)
+    torch.cuda.synchronize()
+    ref = f64(x) @ f64(w).T
+    assert_agree(f64(y), ref, "linear bf16")
+    # fp32 output: only fp32 accumulation-order error
+    np.testing.assert_allclose(f64(yf), ref, rtol=1e-4, atol=1e-4 * np.abs(ref).max())
+
+
+# ---- a2: modulation ----------------------------------------------------------------
+
+def test_modulate(L):
+    vec = syn.cond_vectors(21, 3)
+    lins = [syn.global_weight(22, f"single_stream_modulations.{m}.lin.weight") for m in syn.MODES]
+    say("modulate")
+    mod = L.flux3_modulate(dev(vec), [dev(w) for w in lins])
+    torch.cuda.synchronize()
+    for i in range(3):
+        ref = O.modulation(f64(vec[i]), f64(lins[i]))
+        assert_agree(f64(mod[i]), ref, f"modulate seg {i}", cos_min=0.99999, rel_max=1e-4)
+
+
+# ---- a3: LayerNorm + modulation --------------------------------------------------------
+
+@pytest.mark.parametrize("n,segs", [(1, [0, 1]), (7, [0, 3, 7]), (300, [0, 128, 200, 300])])
+def test_ln_modulate(L, n, segs):
+    x = syn.normal_bf16((n, 3072), 1.0, 31, f"ln.x.{n}") .float().mul_(2.0).add_(0.5).to(torch.bfloat16)
+    nseg = len(segs) - 1
+    mod = syn.normal_f32((nseg, 3, 3072), 0.5, 32, "ln.mod")
+    out = torch.empty((n, 3072), dtype=torch.bfloat16, device="cuda")
+    say(f"ln_modulate n={n}")
+    L.flux3_ln_modulate(dev(x), out, segs, dev(mod))
+    torch.cuda.synchronize()
+    xm = O.layer_norm(f64(x))
+    ref = np.empty_like(xm)
+    for s in range(nseg):
+        a, b = segs[s], segs[s + 1]
+        ref[a:b] = O.modulate(xm[a:b], f64(mod[s, 0]), f64(mod[s, 1]))
+    assert_agree(f64(out), ref, "ln_modulate")
+    # per element: bf16 rounding of the output plus fp32 statistics
+    np.testing.assert_allclose(f64(out), ref, rtol=2 ** -7, atol=1e-2)
+
+
+def test_ln_modulate_scale_minus_one_gives_shift(L):
+    n = 5
+    x = syn.normal_bf16((n, 3072), 1.0, 33, "ln.x2")
+    mod = torch.zeros((1, 3, 3072))
+    mod[0, 0] = syn.normal_f32((3072,), 1.0, 34, "ln.shift")
+    mod[0, 1] = -1.0
+    out = torch.empty((n, 3072), dtype=torch.bfloat16, device="cuda")
+    L.flux3_ln_modulate(dev(x), out, [0, n], dev(mod))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(f64(out), np.broadcast_to(f64(mod[0, 0].to(torch.bfloat16)), (n, 3072)))
+
+
+# ---- a6: QK RMSNorm + RoPE ---------------------------------------------------------------
+
+@pytest.mark.parametrize("lay", [(2, 3, 5, []), (8, 8, 32, [(4, 4)])])
+def test_qk_norm_rope(L, lay):
+    h, w, nt, refs = lay
+    ids = O.build_ids(h, w, nt, refs)
+    n = len(ids)
+    qkv = syn.normal_bf16((n, 9216), 1.5, 41, f"qkv.{n}")
+    sq = syn.uniform_bf16((128,), 0.5, 1.5, 42, "sq")
+    sk = syn.uniform_bf16((128,), 0.5, 1.5, 43, "sk")
+    d = dev(qkv)
+    table = L.flux3_rope_table(dev(torch.tensor(ids, dtype=torch.float32)))
+    say(f"qk_norm_rope n={n}")
+    L.flux3_qk_norm_rope(d[:, :3072], d[:, 3072:6144], dev(sq), dev(sk), table)
+    torch.cuda.synchronize()
+    q = f64(qkv[:, :3072]).reshape(n, 24, 128)
+    k = f64(qkv[:, 3072:6144]).reshape(n, 24, 128)
+    rq = O.apply_rope(O.rms_norm(q, f64(sq)), ids).reshape(n, 3072)
+    rk = O.apply_rope(O.rms_norm(k, f64(sk)), ids).reshape(n, 3072)
+    out = f64(d)
+    assert_agree(out[:, :3072], rq, "q")
+    assert_agree(out[:, 3072:6144], rk, "k")
+    np.testing.assert_allclose(out[:, :6144], np.concatenate([rq, rk], 1), rtol=2 ** -7, atol=2e-2)
+    np.testing.assert_array_equal(out[:, 6144:], f64(qkv[:, 6144:]))   # v untouched
+
+
+# ---- a7: attention -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 7, 64, 130, 300, 513])
+def test_attention(L, n):
+    qkv = syn.normal_bf16((n, 9216), 1.0, 51, f"att.{n}")
+    d = dev(qkv)
+    o = torch.empty((n, 3072), dtype=torch.bfloat16, device="cuda")
+    say(f"attention n={n}")
+    L.flux3_attention(d[:, :3072], d[:, 3072:6144], d[:, 6144:], o)
+    torch.cuda.synchronize()
+    q, k, v = (f64(qkv[:, i * 3072:(i + 1) * 3072]).reshape(n, 24, 128) for i in range(3))
+    # scale q so the softmax is peaked enough to matter
+    ref = O.attention(q, k, v).reshape(n, 3072)
+    assert_agree(f64(o), ref, f"attention n={n}")
+
+
+def test_attention_special_cases(L):
+    n = 200
+    qkv = syn.normal_bf16((n, 9216), 2.0, 52, "att.sp")
+    qkv[:, 6144:] = 1.0                      # V = ones -> O = ones
+    d = dev(qkv)
+    o = torch.empty((n, 3072), dtype=torch.bfloat16, device="cuda")
+    L.flux3_attention(d[:, :3072], d[:, 3072:6144], d[:, 6144:], o)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(f64(o), 1.0, atol=2 ** -7)
+    # one key: O = V of that key
+    o1 = torch.empty((1, 3072), dtype=torch.bfloat16, device="cuda")
+    d1 = dev(syn.normal_bf16((1, 9216), 1.0, 53, "att.one"))
+    L.flux3_attention(d1[:, :3072], d1[:, 3072:6144], d1[:, 6144:], o1)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(f64(o1), f64(d1[:, 6144:]))
+
+
+# ---- a3..a8: one block ------------------------------------------------------------------------
+
+def _block_inputs(seed, lay, mod_scale=0.5):
+    ids = O.build_ids(lay.img_h, lay.img_w, lay.n_txt, lay.refs)
+    n = len(ids)
+    segs = [0] + [b for _, _, b in lay.segments()]
+    w = syn.block_weights(seed, "single_blocks.0")
+    x = syn.block_activations(seed + 1, n)
+    mods = syn.normal_f32((len(segs) - 1, 3, 3072), mod_scale, seed + 2, "mods")
+    return ids, segs, w, x, mods
+
+
+def _run_block(L, ids, segs, w, x, mods):
+    blk = L.PackedBlock(upload(w))
+    table = L.flux3_rope_table(dev(torch.tensor(ids, dtype=torch.float32)))
+    xd = dev(x)
+    ws = L.workspace(L.flux3_block_workspace_size(len(ids)))
+    L.flux3_block_forward(xd, segs, dev(mods), blk, table, ws)
+    torch.cuda.synchronize()
+    return xd
+
+
+@pytest.mark.parametrize("lay", [syn.Layout(8, 8, 32), syn.Layout(5, 6, 13, [(3, 4)]),
+                                 syn.Layout(16, 20, 88, [(8, 24)])])
+def test_block_forward(L, lay):
+    ids, segs, w, x, mods = _block_inputs(61, lay)
+    say(f"block_forward n={len(ids)}")
+    got = _run_block(L, ids, segs, w, x, mods)
+    segs_t = list(zip(segs[:-1], segs[1:]))
+    ref = O.block_forward(f64(x), segs_t, f64(mods), to_f64(w), ids)
+    assert_agree(f64(got), ref, f"block n={len(ids)}")
+    # the update x_out - x must agree too (it is small next to x)
+    assert_agree(f64(got) - f64(x), ref - f64(x), "block update", cos_min=0.999, rel_max=5e-2)
+
+
+def test_block_zero_gate_is_identity(L):
+    lay = syn.Layout(8, 8, 32)
+    ids, segs, w, x, mods = _block_inputs(62, lay)
+    mods[:, 2] = 0.0
+    got = _run_block(L, ids, segs, w, x, mods)
+    np.testing.assert_array_equal(f64(got), f64(x))
+
+
+def test_block_scale_minus_one_is_identity(L):
+    lay = syn.Layout(8, 8, 32)
+    ids, segs, w, x, mods = _block_inputs(63, lay)
+    mods[:, 0] = 0.0
+    mods[:, 1] = -1.0
+    got = _run_block(L, ids, segs, w, x, mods)
+    np.testing.assert_array_equal(f64(got), f64(x))
+
+
+# ---- conditioning -------------------------------------------------------------------------------
+
+def test_time_vectors(L):
+    W = {k: syn.global_weight(71, k) for k in ("time_in.in_layer.weight", "time_in.out_layer.weight",
+                                               "ref_time_in.in_layer.weight", "ref_time_in.out_layer.weight")}
+    Wd = {k: dev(v) for k, v in W.items()}
+    vec = torch.empty((3, 3072), dtype=torch.float32, device="cuda")
+    ws = L.workspace(1 << 20)
+    say("time_vectors")
+    for sig, sig_next in ((0.9652, 0.93), (1.0, 0.5), (0.1, 0.0)):
+        L.flux3_time_vectors(Wd["time_in.in_layer.weight"], Wd["time_in.out_layer.weight"],
+                             Wd["ref_time_in.in_layer.weight"], Wd["ref_time_in.out_layer.weight"],
+                             sig, sig_next, [1, 0, 0], vec, ws)
+        torch.cuda.synchronize()
+        ref = O.mode_vectors(lambda k: f64(W[k]), np.float32(sig), np.float32(sig_next),
+                             ["image", "image_cond", "txt"])
+        for i, m in enumerate(["image", "image_cond", "txt"]):
+            assert_agree(f64(vec[i]), ref[m], f"vec {m} sigma={sig}", cos_min=0.99999, rel_max=1e-3)
+    # base checkpoint: no ref_time_in
+    L.flux3_time_vectors(Wd["time_in.in_layer.weight"], Wd["time_in.out_layer.weight"], None, None,
+                         0.5, 0.0, [1], vec, ws)
+    torch.cuda.synchronize()
+    ref = O.mode_vectors(lambda k: f64(W[k]), 0.5, None, ["image"])["image"]
+    assert_agree(f64(vec[0]), ref, "vec base", cos_min=0.99999, rel_max=1e-3)
+
+
+def test_euler_step(L):
+    x = torch.randn(1000, generator=torch.Generator().manual_seed(0))
+    v = torch.randn(1000, generator=torch.Generator().manual_seed(1))
+    xd, vd = dev(x), dev(v)
+    xb = torch.empty(1000, dtype=torch.bfloat16, device="cuda")
+    L.flux3_euler_step(xd, xb, vd, 0.9, 0.7)
+    torch.cuda.synchronize()
+    ref = O.euler_update(f64(x), f64(v), np.float32(0.9), np.float32(0.7))
+    np.testing.assert_allclose(f64(xd), ref, rtol=1e-6, atol=1e-6)
+    np.testing.assert_array_equal(f64(xb), f64(xd.cpu().to(torch.bfloat16)))
