@@ -175,6 +175,30 @@ int flux3_pack_block(const uint16_t* q_proj, const uint16_t* k_proj, const uint1
                      const uint16_t* attn_out, const uint16_t* mlp_in, const uint16_t* mlp_out,
                      uint16_t* w_in, uint16_t* w_out, hipStream_t stream);
 
+/* ---- a4 + a5: the block's input projections, one fused product ------------------
+ * [q | k | v] = xm [Wq; Wk; Wv]^T and h = silu(a) * b with [a | b] = xm mlp_in^T
+ * ([blog] "Inside one block": q, k, v and the SwiGLU MLP all read the same
+ * modulated input; [issue] "Structure": a, b = mlp_in(x_mod).chunk(2)).
+ *   xm    : device [n][3072] bf16 (modulated input, contiguous rows)
+ *   w_in  : device packed [27648][3072] (flux3_pack_block)
+ *   qkv   : device output [n][9216] bf16 (q | k | v, contiguous rows)
+ *   h     : device output [n][9216] bf16, row stride ldh (>= 9216)
+ */
+int flux3_block_in_proj(const uint16_t* xm, int n, const uint16_t* w_in, uint16_t* qkv, uint16_t* h,
+                        int ldh, hipStream_t stream);
+
+/* ---- a8: the block's output projection and gated residual --------------------------
+ * x <- x + gate[m] * ([o | h] [attn_out | mlp_out]^T), m = segment of the row
+ * ([blog] "Inside one block"; [issue] "Structure": x + gate * (attn_out(attn)
+ * + mlp_out(silu(a) * b))).
+ *   cat   : device [n][12288] bf16 = [o | h] (contiguous rows)
+ *   w_out : device packed [3072][12288] (flux3_pack_block)
+ *   x     : device [n][3072] bf16, updated in place
+ *   seg_off, n_seg, mod : as flux3_block_forward (gate = mod + s*9216 + 6144)
+ */
+int flux3_block_out_proj(const uint16_t* cat, int n, const uint16_t* w_out, uint16_t* x,
+                         const int* seg_off, int n_seg, const float* mod, hipStream_t stream);
+
 /* ---- a3..a8: one block -----------------------------------------------------------
  * x <- x + gate * (attn_out(attention(rope(rms(q)), rope(rms(k)), v)) +
  *                  mlp_out(silu(a) * b)),  with q, k, v, [a|b] projections of

@@ -66,6 +66,8 @@ _SIGS = {
     "flux3_attention": (I, [P, I, P, I, P, I, P, I, I, P]),
     "flux3_linear": (I, [P, I, P, I, P, I, P, I, I, I, P]),
     "flux3_pack_block": (I, [P, P, P, P, P, P, P, P, P]),
+    "flux3_block_in_proj": (I, [P, I, P, P, P, I, P]),
+    "flux3_block_out_proj": (I, [P, I, P, P, P, I, P, P]),
     "flux3_block_workspace_size": (S, [I]),
     "flux3_block_forward": (I, [P, I, P, I, P, C.POINTER(BlockWeightsC), P, P, S, P]),
     "flux3_time_vectors": (I, [P, P, P, P, F, F, P, I, P, P, S, P]),
@@ -217,6 +219,17 @@ class PackedBlock:
         return BlockWeightsC(_ptr(self.w_in), _ptr(self.w_out), _ptr(self.q_scale), _ptr(self.k_scale))
 
 
+def flux3_block_in_proj(xm, w_in, qkv, h, stream=None):
+    _check(lib().flux3_block_in_proj(_ptr(xm), xm.shape[0], _ptr(w_in), _ptr(qkv), _ptr(h), _ld(h),
+                                     _stream(stream)))
+
+
+def flux3_block_out_proj(cat, w_out, x, seg_off, mod, stream=None):
+    arr, n_seg = _segs(seg_off)
+    _check(lib().flux3_block_out_proj(_ptr(cat), cat.shape[0], _ptr(w_out), _ptr(x), arr, n_seg,
+                                      _ptr(mod), _stream(stream)))
+
+
 def flux3_block_workspace_size(n: int) -> int:
     return lib().flux3_block_workspace_size(n)
 
@@ -249,7 +262,10 @@ class ModelWeights:
 
     def __init__(self, glob: dict, early: dict, single: list):
         self.glob, self.early, self.single = glob, early, single
-        n_early = len(next(iter(early.values()))) if early else 0
+        n_early = max((len(v) for v in early.values()), default=0)
+        for m, blocks in early.items():
+            if blocks and len(blocks) != n_early:
+                raise ValueError(f"stream {m} has {len(blocks)} stage-1 blocks, expected {n_early}")
         self._early_arr = {}
         cw = ModelWeightsC()
         g = lambda k: _ptr(glob.get(k))

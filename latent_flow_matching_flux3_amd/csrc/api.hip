@@ -89,38 +89,31 @@ int check_block_weights(const flux3_block_weights* w) {
   return FLUX3_OK;
 }
 
-// a3..a8 with arguments already checked.
-void block_forward_unchecked(bf16* x, int n, const SegTable& seg, const float* mod,
-                             const flux3_block_weights* w, const float* table, const BlockWs& ws,
-                             hipStream_t st) {
-  // a3: h = (1 + scale) LN(x) + shift
-  launch_ln_modulate(x, kHidden, ws.xm, kHidden, n, seg, mod, 3 * kHidden, st);
-  // a4 + a5: [q | k | v] and h_mlp = silu(a) * b in one product over w_in
+// a4 + a5: [q | k | v] and h_mlp = silu(a) * b in one product over w_in.
+void in_proj(const bf16* xm, int n, const bf16* w_in, bf16* qkv, bf16* h, int ldh, hipStream_t st) {
   GemmArgs g{};
-  g.A = ws.xm;
+  g.A = xm;
   g.lda = kHidden;
-  g.B = B(w->w_in);
+  g.B = w_in;
   g.ldb = kHidden;
   g.M = n;
   g.N = kWInRows;
   g.K = kHidden;
   g.epi = GemmEpi::kInProj;
-  g.C = ws.qkv;
+  g.C = qkv;
   g.ldc = 3 * kHidden;
-  g.H = ws.cat + kHidden;
-  g.ldh = kWOutCols;
+  g.H = h;
+  g.ldh = ldh;
   launch_gemm(g, st);
-  // a6: RMSNorm + RoPE on q and k
-  launch_qk_norm_rope(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, n, B(w->q_scale),
-                      B(w->k_scale), table, st);
-  // a7: attention -> first 3072 columns of cat
-  launch_attention(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, ws.qkv + 2 * kHidden,
-                   3 * kHidden, ws.cat, kWOutCols, n, st);
-  // a8: x += gate * ([o | h] [W_o | W_out]^T)
+}
+
+// a8: x += gate * ([o | h] [W_o | W_out]^T).
+void out_proj(const bf16* cat, int n, const bf16* w_out, bf16* x, const SegTable& seg,
+              const float* mod, hipStream_t st) {
   GemmArgs o{};
-  o.A = ws.cat;
+  o.A = cat;
   o.lda = kWOutCols;
-  o.B = B(w->w_out);
+  o.B = w_out;
   o.ldb = kWOutCols;
   o.M = n;
   o.N = kHidden;
@@ -133,6 +126,24 @@ void block_forward_unchecked(bf16* x, int n, const SegTable& seg, const float* m
   o.gate_offset = 2 * kHidden;
   o.seg = seg;
   launch_gemm(o, st);
+}
+
+// a3..a8 with arguments already checked.
+void block_forward_unchecked(bf16* x, int n, const SegTable& seg, const float* mod,
+                             const flux3_block_weights* w, const float* table, const BlockWs& ws,
+                             hipStream_t st) {
+  // a3: h = (1 + scale) LN(x) + shift
+  launch_ln_modulate(x, kHidden, ws.xm, kHidden, n, seg, mod, 3 * kHidden, st);
+  // a4 + a5: q | k | v into qkv; SwiGLU output into the last 9216 columns of cat
+  in_proj(ws.xm, n, B(w->w_in), ws.qkv, ws.cat + kHidden, kWOutCols, st);
+  // a6: RMSNorm + RoPE on q and k
+  launch_qk_norm_rope(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, n, B(w->q_scale),
+                      B(w->k_scale), table, st);
+  // a7: attention -> first 3072 columns of cat
+  launch_attention(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, ws.qkv + 2 * kHidden,
+                   3 * kHidden, ws.cat, kWOutCols, n, st);
+  // a8: gated residual
+  out_proj(ws.cat, n, B(w->w_out), x, seg, mod, st);
 }
 
 }  // namespace
@@ -298,6 +309,34 @@ int flux3_pack_block(const uint16_t* q_proj, const uint16_t* k_proj, const uint1
   launch_pack_block(B(q_proj), B(k_proj), B(v_proj), B(attn_out), B(mlp_in), B(mlp_out), B(w_in),
                     B(w_out), stream);
   return check_launch("pack_block");
+}
+
+int flux3_block_in_proj(const uint16_t* xm, int n, const uint16_t* w_in, uint16_t* qkv, uint16_t* h,
+                        int ldh, hipStream_t stream) {
+  REQUIRE(n >= 0, FLUX3_EINVAL, "n=%d", n);
+  if (n == 0) return FLUX3_OK;
+  REQUIRE_PTR(xm);
+  REQUIRE_PTR(w_in);
+  REQUIRE_PTR(qkv);
+  REQUIRE_PTR(h);
+  REQUIRE_LD(ldh, kMlp);
+  in_proj(B(xm), n, B(w_in), B(qkv), B(h), ldh, stream);
+  return check_launch("block_in_proj");
+}
+
+int flux3_block_out_proj(const uint16_t* cat, int n, const uint16_t* w_out, uint16_t* x,
+                         const int* seg_off, int n_seg, const float* mod, hipStream_t stream) {
+  REQUIRE(n >= 0, FLUX3_EINVAL, "n=%d", n);
+  if (n == 0) return FLUX3_OK;
+  REQUIRE_PTR(cat);
+  REQUIRE_PTR(w_out);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(mod);
+  SegTable seg;
+  int rc = make_segs(seg_off, n_seg, n, &seg);
+  if (rc) return rc;
+  out_proj(B(cat), n, B(w_out), B(x), seg, mod, stream);
+  return check_launch("block_out_proj");
 }
 
 size_t flux3_block_workspace_size(int n) { return n > 0 ? block_ws_bytes(n) : 0; }
