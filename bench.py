@@ -177,7 +177,7 @@ def main():
     xm = torch.empty((n, HIDDEN), dtype=torch.bfloat16, device="cuda")
     qkv = torch.empty((n, 3 * HIDDEN), dtype=torch.bfloat16, device="cuda")
     cat = torch.empty((n, HIDDEN + MLP), dtype=torch.bfloat16, device="cuda")
-    xs = torch.randn((n, HIDDEN), device="cuda").to(torch.bfloat16)
+    xs = torch.randn((n, HIDDEN), device="cuda")
     mod = torch.randn((2, 3, HIDDEN), device="cuda") * 0.1
     segs = [0, n_img, n]
     L.flux3_ln_modulate(xs, xm, segs, mod)

@@ -108,12 +108,13 @@ int flux3_modulate(const float* vec, const uint16_t* const* w_lin, int n_seg, fl
 /* ---- a3: LayerNorm + modulation --------------------------------------------
  * out = (1 + scale[m]) * LN(x) + shift[m], LN without affine, eps 1e-6, where
  * m is the segment of the row ([blog] "Inside one block"; [issue] "Structure").
- *   x, out  : device [n][3072] bf16 (row strides ldx, ldo)
+ *   x       : device [n][3072] fp32 residual stream (row stride ldx)
+ *   out     : device [n][3072] bf16 (row stride ldo)
  *   seg_off : host [n_seg+1] int, 0 = seg_off[0] < ... < seg_off[n_seg] = n
  *   mod     : device, segment s uses shift = mod + s*mod_stride and
  *             scale = shift + 3072 (fp32); mod_stride >= 6144
  */
-int flux3_ln_modulate(const uint16_t* x, int ldx, uint16_t* out, int ldo, int n,
+int flux3_ln_modulate(const float* x, int ldx, uint16_t* out, int ldo, int n,
                       const int* seg_off, int n_seg, const float* mod, int mod_stride,
                       hipStream_t stream);
 
@@ -193,17 +194,19 @@ int flux3_block_in_proj(const uint16_t* xm, int n, const uint16_t* w_in, uint16_
  * + mlp_out(silu(a) * b))).
  *   cat   : device [n][12288] bf16 = [o | h] (contiguous rows)
  *   w_out : device packed [3072][12288] (flux3_pack_block)
- *   x     : device [n][3072] bf16, updated in place
+ *   x     : device [n][3072] fp32 residual stream, updated in place
  *   seg_off, n_seg, mod : as flux3_block_forward (gate = mod + s*9216 + 6144)
  */
-int flux3_block_out_proj(const uint16_t* cat, int n, const uint16_t* w_out, uint16_t* x,
+int flux3_block_out_proj(const uint16_t* cat, int n, const uint16_t* w_out, float* x,
                          const int* seg_off, int n_seg, const float* mod, hipStream_t stream);
 
 /* ---- a3..a8: one block -----------------------------------------------------------
  * x <- x + gate * (attn_out(attention(rope(rms(q)), rope(rms(k)), v)) +
  *                  mlp_out(silu(a) * b)),  with q, k, v, [a|b] projections of
  * h = (1 + scale) LN(x) + shift ([blog] "Inside one block"; [issue] "Structure").
- *   x        : device [n][3072] bf16, updated in place
+ *   x        : device [n][3072] fp32 residual stream, updated in place (the
+ *              residual is kept in fp32 across the 33 blocks; every GEMM
+ *              operand is bf16)
  *   seg_off  : host [n_seg+1] row offsets; segment s uses mod + s*9216
  *              (shift, scale, gate) fp32 (device)
  *   table    : device rope table of these n rows
@@ -211,7 +214,7 @@ int flux3_block_out_proj(const uint16_t* cat, int n, const uint16_t* w_out, uint
  * Attention covers all n rows: a stage-1 call passes one stream's rows.
  */
 size_t flux3_block_workspace_size(int n);
-int flux3_block_forward(uint16_t* x, int n, const int* seg_off, int n_seg, const float* mod,
+int flux3_block_forward(float* x, int n, const int* seg_off, int n_seg, const float* mod,
                         const flux3_block_weights* w, const float* table, void* workspace,
                         size_t ws_bytes, hipStream_t stream);
 

@@ -108,7 +108,7 @@ void in_proj(const bf16* xm, int n, const bf16* w_in, bf16* qkv, bf16* h, int ld
 }
 
 // a8: x += gate * ([o | h] [W_o | W_out]^T).
-void out_proj(const bf16* cat, int n, const bf16* w_out, bf16* x, const SegTable& seg,
+void out_proj(const bf16* cat, int n, const bf16* w_out, float* x, const SegTable& seg,
               const float* mod, hipStream_t st) {
   GemmArgs o{};
   o.A = cat;
@@ -129,7 +129,7 @@ void out_proj(const bf16* cat, int n, const bf16* w_out, bf16* x, const SegTable
 }
 
 // a3..a8 with arguments already checked.
-void block_forward_unchecked(bf16* x, int n, const SegTable& seg, const float* mod,
+void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* mod,
                              const flux3_block_weights* w, const float* table, const BlockWs& ws,
                              hipStream_t st) {
   // a3: h = (1 + scale) LN(x) + shift
@@ -213,7 +213,7 @@ int flux3_modulate(const float* vec, const uint16_t* const* w_lin, int n_seg, fl
   return check_launch("modulate");
 }
 
-int flux3_ln_modulate(const uint16_t* x, int ldx, uint16_t* out, int ldo, int n,
+int flux3_ln_modulate(const float* x, int ldx, uint16_t* out, int ldo, int n,
                       const int* seg_off, int n_seg, const float* mod, int mod_stride,
                       hipStream_t stream) {
   REQUIRE(n >= 0, FLUX3_EINVAL, "n=%d", n);
@@ -227,7 +227,7 @@ int flux3_ln_modulate(const uint16_t* x, int ldx, uint16_t* out, int ldo, int n,
   SegTable seg;
   int rc = make_segs(seg_off, n_seg, n, &seg);
   if (rc) return rc;
-  launch_ln_modulate(B(x), ldx, B(out), ldo, n, seg, mod, mod_stride, stream);
+  launch_ln_modulate(x, ldx, B(out), ldo, n, seg, mod, mod_stride, stream);
   return check_launch("ln_modulate");
 }
 
@@ -324,7 +324,7 @@ int flux3_block_in_proj(const uint16_t* xm, int n, const uint16_t* w_in, uint16_
   return check_launch("block_in_proj");
 }
 
-int flux3_block_out_proj(const uint16_t* cat, int n, const uint16_t* w_out, uint16_t* x,
+int flux3_block_out_proj(const uint16_t* cat, int n, const uint16_t* w_out, float* x,
                          const int* seg_off, int n_seg, const float* mod, hipStream_t stream) {
   REQUIRE(n >= 0, FLUX3_EINVAL, "n=%d", n);
   if (n == 0) return FLUX3_OK;
@@ -335,13 +335,13 @@ int flux3_block_out_proj(const uint16_t* cat, int n, const uint16_t* w_out, uint
   SegTable seg;
   int rc = make_segs(seg_off, n_seg, n, &seg);
   if (rc) return rc;
-  out_proj(B(cat), n, B(w_out), B(x), seg, mod, stream);
+  out_proj(B(cat), n, B(w_out), x, seg, mod, stream);
   return check_launch("block_out_proj");
 }
 
 size_t flux3_block_workspace_size(int n) { return n > 0 ? block_ws_bytes(n) : 0; }
 
-int flux3_block_forward(uint16_t* x, int n, const int* seg_off, int n_seg, const float* mod,
+int flux3_block_forward(float* x, int n, const int* seg_off, int n_seg, const float* mod,
                         const flux3_block_weights* w, const float* table, void* workspace,
                         size_t ws_bytes, hipStream_t stream) {
   REQUIRE(n >= 0, FLUX3_EINVAL, "n=%d", n);
@@ -357,7 +357,7 @@ int flux3_block_forward(uint16_t* x, int n, const int* seg_off, int n_seg, const
   REQUIRE(workspace != nullptr && aligned16(workspace), FLUX3_EWORKSPACE, "workspace missing or misaligned");
   REQUIRE(ws_bytes >= block_ws_bytes(n), FLUX3_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes,
           block_ws_bytes(n));
-  block_forward_unchecked(B(x), n, seg, mod, w, table, carve_block_ws(workspace, n), stream);
+  block_forward_unchecked(x, n, seg, mod, w, table, carve_block_ws(workspace, n), stream);
   return check_launch("block_forward");
 }
 
@@ -410,7 +410,7 @@ int time_vectors_unchecked(const uint16_t* w1, const uint16_t* w2, const uint16_
 
 // Stack workspace layout.
 struct StackWs {
-  bf16* x;          // [N][3072] residual stream, tokens image | image_cond | txt
+  float* x;         // [N][3072] fp32 residual stream, tokens image | image_cond | txt
   float* vec;       // [3][3072]
   float* mod_early; // [3][9216]
   float* mod_single;// [3][9216]
@@ -421,7 +421,7 @@ struct StackWs {
 };
 
 size_t stack_ws_bytes(int n_total) {
-  return align256((size_t)n_total * kHidden * 2) + align256(3 * kHidden * 4) +
+  return align256((size_t)n_total * kHidden * 4) + align256(3 * kHidden * 4) +
          2 * align256(3 * 3 * kHidden * 4) + align256(2 * kHidden * 4) + align256(kTimeWsBytes) +
          block_ws_bytes(n_total);
 }
@@ -429,8 +429,8 @@ size_t stack_ws_bytes(int n_total) {
 StackWs carve_stack_ws(void* ws, int n_total) {
   char* p = (char*)ws;
   StackWs s;
-  s.x = (bf16*)p;
-  p += align256((size_t)n_total * kHidden * 2);
+  s.x = (float*)p;
+  p += align256((size_t)n_total * kHidden * 4);
   s.vec = (float*)p;
   p += align256(3 * kHidden * 4);
   s.mod_early = (float*)p;
@@ -576,7 +576,7 @@ int flux3_stack_forward(const flux3_model_weights* w, const uint16_t* img, int n
     g.M = counts[i];
     g.N = kHidden;
     g.K = in_dim[m];
-    g.epi = GemmEpi::kStoreBf16;
+    g.epi = GemmEpi::kStoreF32;
     g.C = s.x + (size_t)row0[i] * kHidden;
     g.ldc = kHidden;
     launch_gemm(g, stream);

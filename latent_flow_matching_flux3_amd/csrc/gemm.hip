@@ -101,7 +101,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::F
       break;
     }
     case GemmEpi::kGatedResidual: {
-      bf16* X = (bf16*)g.C;
+      float* X = (float*)g.C;
 #pragma unroll
       for (int i = 0; i < T::FM; ++i)
 #pragma unroll
@@ -112,8 +112,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::F
 #pragma unroll
             for (int j = 0; j < T::FN; ++j) {
               const int col = wcol0 + 32 * j + lc;
-              bf16* px = X + (size_t)row * g.ldc + col;
-              *px = to_bf16((float)*px + gate[col] * acc[i][j][r]);
+              float* px = X + (size_t)row * g.ldc + col;
+              *px = *px + gate[col] * acc[i][j][r];
             }
           }
         }

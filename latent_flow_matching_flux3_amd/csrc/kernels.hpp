@@ -16,7 +16,7 @@ enum class GemmEpi {
   kStoreBf16,     // C bf16 [M][N], stride ldc
   kStoreF32,      // C fp32 [M][N], stride ldc
   kInProj,        // cols < 9216: q|k|v store; cols >= 9216: SwiGLU of interleaved a/b -> h
-  kGatedResidual  // x[row][col] += gate[seg(row)][col] * acc
+  kGatedResidual  // x[row][col] += gate[seg(row)][col] * acc, x fp32
 };
 
 struct GemmArgs {
@@ -39,7 +39,7 @@ struct GemmArgs {
   SegTable seg;
 };
 
-void launch_ln_modulate(const bf16* x, int ldx, bf16* out, int ldo, int n, const SegTable& seg,
+void launch_ln_modulate(const float* x, int ldx, bf16* out, int ldo, int n, const SegTable& seg,
                         const float* mod, int mod_stride, hipStream_t st);
 void launch_rope_table(const float* ids, int n, float* table, hipStream_t st);
 void launch_qk_norm_rope(bf16* q, int ldq, bf16* k, int ldk, int n, const bf16* q_scale,

@@ -13,14 +13,15 @@
 namespace flux3 {
 
 // ---------------------------------------------------------------------------
-// K1: one wave per row.  A row of 3072 bf16 is 384 chunks of 16 bytes; lane l
-// owns chunks l, l+64, ..., l+320 (coalesced 1 KiB per wave instruction) and
-// keeps its 48 values in registers, so the row is read once and the variance
-// is the exact two-pass form mean((x - mu)^2) in fp32.
+// K1: one wave per row of the fp32 residual stream.  A row of 3072 floats is
+// 768 chunks of 16 bytes; lane l owns chunks l, l+64, ..., l+704 (coalesced
+// 1 KiB per wave instruction) and keeps its 48 values in registers, so the
+// row is read once and the variance is the exact two-pass form
+// mean((x - mu)^2) in fp32.  Output bf16 (the GEMM operand).
 // ---------------------------------------------------------------------------
 constexpr int kLnRowsPerBlock = 4;
 
-__global__ __launch_bounds__(256) void ln_modulate_kernel(const bf16* __restrict__ x, int ldx,
+__global__ __launch_bounds__(256) void ln_modulate_kernel(const float* __restrict__ x, int ldx,
                                                           bf16* __restrict__ out, int ldo, int n,
                                                           SegTable seg,
                                                           const float* __restrict__ mod,
@@ -28,25 +29,25 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const bf16* __restrict
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kLnRowsPerBlock + (threadIdx.x >> 6);
   if (row >= n) return;
-  const bf16* xr = x + (size_t)row * ldx;
-  float v[6][8];
+  const float* xr = x + (size_t)row * ldx;
+  float v[12][4];
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    bf16x8 c = *(const bf16x8*)(xr + (lane + 64 * i) * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v[i][e] = (float)c[e];
-      s += v[i][e];
-    }
+  for (int i = 0; i < 12; ++i) {
+    const float4 c = *(const float4*)(xr + (lane + 64 * i) * 4);
+    v[i][0] = c.x;
+    v[i][1] = c.y;
+    v[i][2] = c.z;
+    v[i][3] = c.w;
+    s += (c.x + c.y) + (c.z + c.w);
   }
   const float mu = wave_sum(s) * (1.0f / kHidden);
   float q = 0.f;
 #pragma unroll
-  for (int i = 0; i < 6; ++i)
+  for (int i = 0; i < 12; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float d = v[i][e] - mu;
+    for (int e = 0; e < 4; ++e) {
+      const float d = v[i][e] - mu;
       q += d * d;
     }
   const float var = wave_sum(q) * (1.0f / kHidden);
@@ -55,20 +56,20 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const bf16* __restrict
   const float* scale = shift + kHidden;
   bf16* orow = out + (size_t)row * ldo;
 #pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    const int c0 = (lane + 64 * i) * 8;
-    const float4 sh0 = *(const float4*)(shift + c0), sh1 = *(const float4*)(shift + c0 + 4);
-    const float4 sc0 = *(const float4*)(scale + c0), sc1 = *(const float4*)(scale + c0 + 4);
-    const float sh[8] = {sh0.x, sh0.y, sh0.z, sh0.w, sh1.x, sh1.y, sh1.z, sh1.w};
-    const float sc[8] = {sc0.x, sc0.y, sc0.z, sc0.w, sc1.x, sc1.y, sc1.z, sc1.w};
-    bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = to_bf16((1.0f + sc[e]) * ((v[i][e] - mu) * rstd) + sh[e]);
-    *(bf16x8*)(orow + c0) = o;
+  for (int i = 0; i < 12; ++i) {
+    const int c0 = (lane + 64 * i) * 4;
+    const float4 sh = *(const float4*)(shift + c0);
+    const float4 sc = *(const float4*)(scale + c0);
+    bf16x4 o;
+    o[0] = to_bf16((1.0f + sc.x) * ((v[i][0] - mu) * rstd) + sh.x);
+    o[1] = to_bf16((1.0f + sc.y) * ((v[i][1] - mu) * rstd) + sh.y);
+    o[2] = to_bf16((1.0f + sc.z) * ((v[i][2] - mu) * rstd) + sh.z);
+    o[3] = to_bf16((1.0f + sc.w) * ((v[i][3] - mu) * rstd) + sh.w);
+    *(bf16x4*)(orow + c0) = o;
   }
 }
 
-void launch_ln_modulate(const bf16* x, int ldx, bf16* out, int ldo, int n, const SegTable& seg,
+void launch_ln_modulate(const float* x, int ldx, bf16* out, int ldo, int n, const SegTable& seg,
                         const float* mod, int mod_stride, hipStream_t st) {
   if (n <= 0) return;
   dim3 grid((n + kLnRowsPerBlock - 1) / kLnRowsPerBlock);

@@ -44,7 +44,7 @@ def test_block_full_size_sampled(L, name):
     say(f"block full size {name} n={n}")
     blk = L.PackedBlock(upload(w))
     table = L.flux3_rope_table(dev(torch.tensor(ids, dtype=torch.float32)))
-    xd = dev(x)
+    xd = dev(x).float()     # fp32 residual stream holding the bf16 draw
     ws = L.workspace(L.flux3_block_workspace_size(n))
     L.flux3_block_forward(xd, segs, dev(mods), blk, table, ws)
     torch.cuda.synchronize()
