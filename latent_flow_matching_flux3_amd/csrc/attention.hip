@@ -34,7 +34,14 @@ constexpr int kBKV = 64;   // keys per tile
 constexpr int kKsChunks = kBKV * 16;     // 16-byte chunks of a K tile
 constexpr int kVtChunks = kHeadDim * 16; // 8-byte chunks of a V^T tile
 
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 15; }
+// LDS swizzles (64 banks x 4 bytes: a 128-bit read serves 16 lanes per cycle,
+// a 64-bit read 32 lanes).  K rows are 256 bytes = 16 chunks of 16 bytes and
+// an operand read puts 16 consecutive rows in one group: chunk c ^ (row & 15).
+// V^T rows are 128 bytes = 16 chunks of 8 bytes and a read puts 32
+// consecutive d in one group, d and d+1 in opposite 128-byte halves:
+// chunk c ^ ((d >> 1) & 15).
+__device__ __forceinline__ int k_swz(int row) { return row & 15; }
+__device__ __forceinline__ int vt_swz(int d) { return (d >> 1) & 15; }
 
 __global__ __launch_bounds__(256) void attn_fwd_kernel(const bf16* __restrict__ q, int ldq,
                                                        const bf16* __restrict__ k, int ldk,
@@ -83,7 +90,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const bf16* __restrict__ 
     for (int i = 0; i < 4; ++i) {
       const int id = tid + 256 * i;
       const int row = id >> 4, c = id & 15;
-      ks_lds[buf][row * 16 + (c ^ (row & 7))] = rk[i];
+      ks_lds[buf][row * 16 + (c ^ k_swz(row))] = rk[i];
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -124,7 +131,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const bf16* __restrict__ 
       const int row = kb * 32 + lr;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8 a = ks_lds[buf][row * 16 + ((2 * s + lh) ^ (row & 7))];
+        const bf16x8 a = ks_lds[buf][row * 16 + ((2 * s + lh) ^ k_swz(row))];
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
       }
     }

@@ -1,0 +1,465 @@
+// bf16 MFMA GEMM kernels  C = A B^T  (A [M][K], B [N][K], both K-contiguous)
+// with the fused epilogues of the block.  Included by gemm.hip only.
+//
+// Both kernels use v_mfma_f32_32x32x16_bf16 on 64-wide waves: each lane feeds
+// one 16-byte LDS read per operand per 16-wide k step.
+//
+//   gemm_regs_kernel : global -> VGPR -> LDS staging, two LDS buffers of
+//                      64-wide K slices (small and odd shapes).
+//   gemm_ring_kernel : global -> LDS directly (global_load_lds_dwordx4) into a
+//                      ring of K slices, software-pipelined so the MFMA pipe
+//                      never waits on a barrier or an LDS read (the large
+//                      projections).
+//
+// LDS bank layout (gfx950: 64 banks x 4 bytes, a 128-bit read serves 16 lanes
+// per cycle).  An MFMA operand read puts 16 consecutive rows, same logical
+// 16-byte chunk, into one 16-lane group, so the chunk index is XOR-swizzled by
+// a function of the row that gives those 16 rows 16 distinct 16-byte slots of
+// the 256-byte bank line.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace flux3 {
+namespace gemm {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gmem_void_t;
+
+// Rows of a K slice of width BK hold CPR = BK/8 chunks of 16 bytes; RPL rows
+// share a 256-byte bank line.  Chunk c of row r lives at c ^ swz(r).
+template <int BK>
+struct Layout {
+  static constexpr int CPR = BK / 8;
+  static constexpr int RPL = 16 / CPR;
+  static constexpr int RPB = 64 / CPR;  // rows per 1 KiB (one wave-wide 16-byte access)
+  __device__ static __forceinline__ int swz(int row) { return (row / RPL) % CPR; }
+};
+
+// One 32x32x16 step of a fragment, computed transposed: the MFMA's A operand
+// is the weight fragment and its B operand the activation fragment, so the
+// accumulator holds C^T.  Accumulator element r of lane l is then
+//   output row = l % 32,  output col = 8 * (r / 4) + 4 * (l / 32) + r % 4,
+// i.e. each lane owns one output row and 4 consecutive columns per group of
+// 4 registers, which the epilogue stores as one 8- or 16-byte access.
+__device__ __forceinline__ floatx16 mma(const bf16x8& x_frag, const bf16x8& w_frag, floatx16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(w_frag, x_frag, acc, 0, 0, 0);
+}
+__device__ __forceinline__ int frag_col(int g4, int lane) { return 8 * g4 + 4 * (lane >> 5); }
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int WTM = BM / WM;
+  static constexpr int WTN = BN / WN;
+  static constexpr int FM = WTM / 32;
+  static constexpr int FN = WTN / 32;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 fragments");
+};
+
+// Tile order: XCD-contiguous bands of the tile grid (workgroups are dealt to
+// the 8 XCDs round-robin), then groups of 4 tile rows, so the tiles running
+// at the same time on one XCD share A rows and B rows in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  int lin = blockIdx.x;
+  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  constexpr int GM = 4;
+  const int group = lin / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int in_group = lin - group * GM * tiles_n;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+template <class T>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::FM][T::FN],
+                                         int wrow0, int wcol0, int lane) {
+  const int lr = lane & 31;
+  switch (g.epi) {
+    case GemmEpi::kStoreBf16:
+    case GemmEpi::kInProj: {
+      if (g.epi == GemmEpi::kStoreBf16 || wcol0 < 3 * kHidden) {
+        bf16* C = (bf16*)g.C;
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) {
+          const int row = wrow0 + 32 * i + lr;
+          if (row < g.M) {
+            bf16* crow = C + (size_t)row * g.ldc + wcol0;
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+              for (int g4 = 0; g4 < 4; ++g4) {
+                bf16x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = to_bf16(acc[i][j][4 * g4 + e]);
+                *(bf16x4*)(crow + 32 * j + frag_col(g4, lane)) = v;
+              }
+          }
+        }
+      } else {
+        // SwiGLU: fragment 2p holds a-columns, 2p+1 the matching b-columns.
+        static_assert(T::FN % 2 == 0, "SwiGLU needs fragment pairs");
+        const int hcol0 = (wcol0 - 3 * kHidden) / 2;
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) {
+          const int row = wrow0 + 32 * i + lr;
+          if (row < g.M) {
+            bf16* hrow = g.H + (size_t)row * g.ldh + hcol0;
+#pragma unroll
+            for (int p = 0; p < T::FN / 2; ++p)
+#pragma unroll
+              for (int g4 = 0; g4 < 4; ++g4) {
+                bf16x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float a = acc[i][2 * p][4 * g4 + e], b = acc[i][2 * p + 1][4 * g4 + e];
+                  v[e] = to_bf16(silu_f(a) * b);
+                }
+                *(bf16x4*)(hrow + 32 * p + frag_col(g4, lane)) = v;
+              }
+          }
+        }
+      }
+      break;
+    }
+    case GemmEpi::kStoreF32: {
+      float* C = (float*)g.C;
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) {
+        const int row = wrow0 + 32 * i + lr;
+        if (row < g.M) {
+          float* crow = C + (size_t)row * g.ldc + wcol0;
+#pragma unroll
+          for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+              *(float4*)(crow + 32 * j + frag_col(g4, lane)) =
+                  make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                              acc[i][j][4 * g4 + 3]);
+        }
+      }
+      break;
+    }
+    case GemmEpi::kGatedResidual: {
+      float* X = (float*)g.C;
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) {
+        const int row = wrow0 + 32 * i + lr;
+        if (row < g.M) {
+          const float* gate = g.mod + (size_t)seg_of_row(g.seg, row) * g.mod_stride + g.gate_offset + wcol0;
+          float* xrow = X + (size_t)row * g.ldc + wcol0;
+#pragma unroll
+          for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int c = 32 * j + frag_col(g4, lane);
+              const float4 gt = *(const float4*)(gate + c);
+              float4 xv = *(const float4*)(xrow + c);
+              xv.x += gt.x * acc[i][j][4 * g4];
+              xv.y += gt.y * acc[i][j][4 * g4 + 1];
+              xv.z += gt.z * acc[i][j][4 * g4 + 2];
+              xv.w += gt.w * acc[i][j][4 * g4 + 3];
+              *(float4*)(xrow + c) = xv;
+            }
+        }
+      }
+      break;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Register-staged kernel (64-wide K slices, two LDS buffers, one barrier per
+// slice).
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_regs_kernel(GemmArgs g, int tiles_m,
+                                                                int tiles_n) {
+  using T = Tile<BM, BN, WM, WN>;
+  using Lay = Layout<64>;
+  constexpr int ACH = BM * 8 / T::NT;  // 16-byte chunks of A per thread per slice
+  constexpr int BCH = BN * 8 / T::NT;
+  constexpr int STAGE = (BM + BN) * 8;
+  static_assert((BM * 8) % T::NT == 0 && (BN * 8) % T::NT == 0, "slice must split evenly");
+  __shared__ bf16x8 lds[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // Global -> register staging addresses (rows of A clamped to M-1).
+  const bf16* a_src[ACH];
+  int a_lds[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    const int id = tid + i * T::NT;
+    const int row = id >> 3, c = id & 7;
+    const int grow = min(m0 + row, g.M - 1);
+    a_src[i] = g.A + (size_t)grow * g.lda + c * 8;
+    a_lds[i] = row * 8 + (c ^ Lay::swz(row));
+  }
+  const bf16* b_src[BCH];
+  int b_lds[BCH];
+#pragma unroll
+  for (int i = 0; i < BCH; ++i) {
+    const int id = tid + i * T::NT;
+    const int row = id >> 3, c = id & 7;
+    b_src[i] = g.B + (size_t)(n0 + row) * g.ldb + c * 8;
+    b_lds[i] = BM * 8 + row * 8 + (c ^ Lay::swz(row));
+  }
+
+  floatx16 acc[T::FM][T::FN];
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  bf16x8 ra[ACH], rb[BCH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) ra[i] = *(const bf16x8*)a_src[i];
+#pragma unroll
+  for (int i = 0; i < BCH; ++i) rb[i] = *(const bf16x8*)b_src[i];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) lds[a_lds[i]] = ra[i];
+#pragma unroll
+  for (int i = 0; i < BCH; ++i) lds[b_lds[i]] = rb[i];
+  __syncthreads();
+
+  const int lr = lane & 31, lh = lane >> 5;
+  int a_off[T::FM], b_off[T::FN];
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) a_off[i] = (wm * T::WTM + 32 * i + lr) * 8;
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j) b_off[j] = BM * 8 + (wn * T::WTN + 32 * j + lr) * 8;
+  const int sw = Lay::swz(lr);  // rows read by this lane are 32 k + lr
+
+  const int KT = g.K / 64;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = (kt & 1) * STAGE;
+    if (kt + 1 < KT) {
+      const int koff = (kt + 1) * 64;
+#pragma unroll
+      for (int i = 0; i < ACH; ++i) ra[i] = *(const bf16x8*)(a_src[i] + koff);
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) rb[i] = *(const bf16x8*)(b_src[i] + koff);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = (2 * ks + lh) ^ sw;
+      bf16x8 af[T::FM], bfr[T::FN];
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) af[i] = lds[cur + a_off[i] + ch];
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) bfr[j] = lds[cur + b_off[j] + ch];
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+          acc[i][j] = mma(af[i], bfr[j], acc[i][j]);
+    }
+    // Buffer cur ^ 1 was last read before the previous barrier.
+    if (kt + 1 < KT) {
+      const int nxt = STAGE - cur;
+#pragma unroll
+      for (int i = 0; i < ACH; ++i) lds[nxt + a_lds[i]] = ra[i];
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) lds[nxt + b_lds[i]] = rb[i];
+    }
+    __syncthreads();
+  }
+
+  epilogue<T>(g, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Ring kernel.
+//
+// STAGES LDS buffers hold K slices of width BK; slice s lives in buffer
+// s % STAGES.  Each global_load_lds_dwordx4 of a wave fills one KiB of a
+// buffer (RPB rows); lane t lands at chunk t of that KiB (row t / CPR,
+// physical chunk t % CPR), so it fetches logical chunk (t % CPR) ^ swz(row).
+//
+// Per slice kt (KSTEPS = BK/16 MFMA steps of FM x FN MFMAs per wave):
+//   steps 0 .. KSTEPS-2 : read the fragments of the next step, then the MFMAs
+//                         of this step (the reads hide behind the MFMAs);
+//   before the last step: wait until this wave's copy of slice kt+1 landed,
+//                         barrier (slice kt+1 visible to all; everyone has
+//                         read all of slice kt), read the first fragments of
+//                         slice kt+1, then the last MFMAs of slice kt with the
+//                         refill of buffer kt % STAGES (slice kt + STAGES)
+//                         issued one load per MFMA between them.
+// So the MFMA pipe only waits on the barrier itself; STAGES-2 slices are in
+// flight while a slice is consumed.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most n_after * PER loads of this wave are outstanding.
+template <int PER, int MAXN>
+__device__ __forceinline__ void wait_slices(int n_after) {
+  if constexpr (MAXN >= 3) {
+    if (n_after >= 3) { wait_vmcnt<3 * PER>(); return; }
+  }
+  if constexpr (MAXN >= 2) {
+    if (n_after == 2) { wait_vmcnt<2 * PER>(); return; }
+  }
+  if constexpr (MAXN >= 1) {
+    if (n_after == 1) { wait_vmcnt<PER>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WAVES_PER_EU>
+__global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
+void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+  using T = Tile<BM, BN, WM, WN>;
+  using Lay = Layout<BK>;
+  constexpr int NW = WM * WN;
+  constexpr int CPR = Lay::CPR;
+  constexpr int STAGE = (BM + BN) * CPR;     // 16-byte chunks per buffer
+  constexpr int A_BLK = BM / Lay::RPB / NW;  // KiB blocks of A per wave per slice
+  constexpr int B_BLK = BN / Lay::RPB / NW;
+  constexpr int PER = A_BLK + B_BLK;         // loads per wave per slice
+  constexpr int KSTEPS = BK / 16;
+  constexpr int NMF = T::FM * T::FN;         // MFMAs per step
+  static_assert(BM % (Lay::RPB * NW) == 0 && BN % (Lay::RPB * NW) == 0, "rows must split over waves");
+  static_assert((STAGES - 1) * PER < 64 && STAGES >= 2 && STAGES <= 4, "ring depth");
+  static_assert(KSTEPS >= 2, "BK >= 32");
+  __shared__ bf16x8 lds[STAGES * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // Source pointers of this lane for each of its PER loads (A rows clamped).
+  const int sub_row = lane / CPR;
+  const bf16* src[PER];
+#pragma unroll
+  for (int i = 0; i < A_BLK; ++i) {
+    const int b = wave * A_BLK + i;
+    const int row = b * Lay::RPB + sub_row;
+    src[i] = g.A + (size_t)min(m0 + row, g.M - 1) * g.lda + ((lane % CPR) ^ Lay::swz(row)) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_BLK; ++i) {
+    const int b = wave * B_BLK + i;
+    const int row = b * Lay::RPB + sub_row;
+    src[A_BLK + i] = g.B + (size_t)(n0 + row) * g.ldb + ((lane % CPR) ^ Lay::swz(row)) * 8;
+  }
+  auto load_one = [&](int q, int slot, int koff) {
+    const int blk = q < A_BLK ? wave * A_BLK + q : BM / Lay::RPB + wave * B_BLK + (q - A_BLK);
+    __builtin_amdgcn_global_load_lds((const gmem_void_t*)(src[q] + koff),
+                                     (lds_void_t*)(lds + slot * STAGE + blk * 64), 16, 0, 0);
+  };
+
+  floatx16 acc[T::FM][T::FN];
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int lr = lane & 31, lh = lane >> 5;
+  const int sw = Lay::swz(lr);  // rows read by this lane are 32 k + lr
+  const int a_base = (wm * T::WTM + lr) * CPR;
+  const int b_base = BM * CPR + (wn * T::WTN + lr) * CPR;
+  bf16x8 af[2][T::FM], bfr[2][T::FN];
+  auto read_frags = [&](int buf, int ks, int p) {
+    const int ch = (2 * ks + lh) ^ sw;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) af[p][i] = lds[buf + a_base + i * 32 * CPR + ch];
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) bfr[p][j] = lds[buf + b_base + j * 32 * CPR + ch];
+  };
+
+  static_assert(KSTEPS % 2 == 0, "the next slice's first fragments land in slot 0");
+  auto mfma_step = [&](int p) {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+        acc[i][j] = mma(af[p][i], bfr[p][j], acc[i][j]);
+  };
+  // Steps 0 .. KSTEPS-2 of the slice in buffer `cur`.  The fragments of the
+  // current step were read a whole step earlier; waiting for them before
+  // issuing the next reads keeps at most FM + FN reads outstanding (lgkmcnt
+  // only counts to 15) and costs nothing.
+  auto inner_steps = [&](int cur) {
+#pragma unroll
+    for (int ks = 0; ks + 1 < KSTEPS; ++ks) {
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
+      read_frags(cur, ks + 1, (ks & 1) ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(ks & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  const int KT = g.K / BK;  // >= 1
+  // Every iteration issues exactly PER loads (the last STAGES of them reload
+  // the final slice into buffers that are no longer read), so the number of
+  // loads in flight behind a given slice is constant.
+  auto slice_off = [&](int s) { return min(s, KT - 1) * BK; };
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) load_one(q, s, slice_off(s));
+  }
+  wait_vmcnt<(STAGES - 1) * PER>();
+  __syncthreads();
+  // Nothing but LDS reads may be pending on lgkmcnt inside the loop (a pending
+  // scalar load would force full waits), so settle the scalar loads here.
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
+  read_frags(0, 0, 0);
+
+  constexpr int pl = (KSTEPS - 1) & 1;  // fragment slot of the last step (1)
+  for (int kt = 0; kt + 1 < KT; ++kt) {
+    const int cur = (kt % STAGES) * STAGE;
+    inner_steps(cur);
+    // Slice kt+1 landed for this wave (STAGES-2 slices issued after it), and
+    // after the barrier for every wave; everyone has read all of slice kt.
+    wait_vmcnt<(STAGES - 2) * PER>();
+    __syncthreads();
+    read_frags(((kt + 1) % STAGES) * STAGE, 0, pl ^ 1);
+    const int koff = slice_off(kt + STAGES);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) {
+        acc[i][j] = mma(af[pl][i], bfr[pl][j], acc[i][j]);
+#pragma unroll
+        for (int q = i * T::FN + j; q < PER; q += NMF) load_one(q, kt % STAGES, koff);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Last slice.
+  inner_steps(((KT - 1) % STAGES) * STAGE);
+  mfma_step(pl);
+  // No load may still be writing LDS when the workgroup ends.
+  wait_vmcnt<0>();
+
+  epilogue<T>(g, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
+}
+
+}  // namespace gemm
+}  // namespace flux3
