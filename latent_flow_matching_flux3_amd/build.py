@@ -36,13 +36,22 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-file code-generation options.  attention.hip keeps every MFMA
+# accumulator in ordinary VGPRs (its softmax reads the score accumulators
+# with VALU instructions; with AGPR accumulators the compiler shuttles them
+# through v_accvgpr_read/write on every tile).
+FILE_FLAGS = {
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

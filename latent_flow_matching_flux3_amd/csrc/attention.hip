@@ -5,21 +5,26 @@
 //
 // Design (gfx950, head_dim 128):
 //   - One workgroup = 4 waves = 128 query rows of one head; each wave owns 32
-//     query rows.  K/V are walked in 64-key tiles staged through LDS (two
-//     buffers, register prefetch of the next tile while the current one is
-//     consumed).
+//     query rows.  K and V are walked in 64-key tiles through a 4-slot LDS
+//     ring, filled straight from global memory (global_load_lds_dwordx4),
+//     three tiles ahead.
 //   - Scores are formed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: A = K from LDS, B = Q^T held in registers for
 //     the whole kernel.  A lane then holds one query row (lane % 32) and 32 of
 //     the tile's 64 keys, so the row max and row sum are per-lane register
-//     reductions plus one exchange with lane ^ 32.
+//     reductions plus one exchange between the wave halves.
 //   - The probabilities stay in registers and feed O^T = V^T P^T directly as
 //     the B operand (their register layout is already the B layout, with the
-//     keys in a fixed permutation that the V^T reads follow).  V is stored
-//     transposed in LDS ([d][key], 8-byte chunks XOR-swizzled by d) so each
-//     A-operand read is two 8-byte LDS loads.
-//   - Online softmax in base 2: p = exp2(s * log2(e)/sqrt(128) - m); the
-//     accumulator is rescaled by exp2(m_old - m_new) when the row max grows.
+//     keys in a fixed permutation).  V stays row-major in LDS; the A operand
+//     V^T is read with ds_read_b64_tr_b16, whose 16-lane transpose hands each
+//     lane 4 keys of one head dim, in exactly that key permutation.
+//   - Software pipeline inside each wave: the scores of tile t+1 (MFMA) are
+//     computed while the softmax of tile t (VALU) runs.
+//   - Online softmax in base 2: p = exp2(s * log2(e)/sqrt(128) - m), where the
+//     reference m may lag the running row max by up to 8 (p <= 256, exact in
+//     the final O / l); the output accumulator is rescaled only when some
+//     row's max jumps past that (a wave-uniform test), i.e. almost never
+//     after the first tile.
 //   - Workgroups of the same head are placed on the same XCD (3 heads per
 //     XCD), so that head's K/V stay in that XCD's L2.
 #include "common.hpp"
@@ -31,25 +36,40 @@ namespace {
 
 constexpr int kBQ = 128;   // query rows per workgroup
 constexpr int kBKV = 64;   // keys per tile
-constexpr int kKsChunks = kBKV * 16;     // 16-byte chunks of a K tile
-constexpr int kVtChunks = kHeadDim * 16; // 8-byte chunks of a V^T tile
+constexpr int kNBuf = 4;   // LDS ring slots
+constexpr int kTileChunks = kBKV * 16;  // 16-byte chunks of a 64 x 128 bf16 tile (16 KiB)
+constexpr float kSlack = 8.0f;          // allowed lag of the softmax reference max (log2 units)
 
-// LDS swizzles (64 banks x 4 bytes: a 128-bit read serves 16 lanes per cycle,
-// a 64-bit read 32 lanes).  K rows are 256 bytes = 16 chunks of 16 bytes and
-// an operand read puts 16 consecutive rows in one group: chunk c ^ (row & 15).
-// V^T rows are 128 bytes = 16 chunks of 8 bytes and a read puts 32
-// consecutive d in one group, d and d+1 in opposite 128-byte halves:
-// chunk c ^ ((d >> 1) & 15).
-__device__ __forceinline__ int k_swz(int row) { return row & 15; }
-__device__ __forceinline__ int vt_swz(int d) { return (d >> 1) & 15; }
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gmem_void_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short short4_t;
 
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const bf16* __restrict__ q, int ldq,
-                                                       const bf16* __restrict__ k, int ldk,
-                                                       const bf16* __restrict__ v, int ldv,
-                                                       bf16* __restrict__ o, int ldo, int n,
-                                                       float scale_log2) {
-  __shared__ bf16x8 ks_lds[2][kKsChunks];
-  __shared__ bf16x4 vt_lds[2][kVtChunks];
+// LDS layouts (64 banks x 4 bytes).  Rows are keys, 256 bytes = 16 chunks of
+// 16 bytes.
+//   K: an operand read puts 16 consecutive rows, same logical chunk, in one
+//      16-lane group: chunk c of row r at c ^ (r & 15).
+//   V: a transpose read by 32 lanes touches 4 key rows (keys 4a .. 4a+3),
+//      64 bytes each at the same offset: the 64-byte quarter q of row r is
+//      stored at q ^ (r & 3), i.e. 16-byte chunk c at c ^ 4 (r & 3).
+__device__ __forceinline__ int k_phys(int row, int c) { return row * 16 + (c ^ (row & 15)); }
+__device__ __forceinline__ int v_phys(int row, int c) { return row * 16 + (c ^ (4 * (row & 3))); }
+
+__device__ __forceinline__ float half_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
+__device__ __forceinline__ float half_sum(float x) { return x + __shfl_xor(x, 32, 64); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict__ k, int ldk,
+                     const bf16* __restrict__ v, int ldv, bf16* __restrict__ o, int ldo, int n,
+                     float scale_log2) {
+  __shared__ bf16x8 ks_lds[kNBuf][kTileChunks];
+  __shared__ bf16x8 vs_lds[kNBuf][kTileChunks];
+  __shared__ bf16x8 qs_lds[kBQ * 16];  // this workgroup's queries, 32 KiB
 
   const int nqb = (n + kBQ - 1) / kBQ;
   const int total = nqb * kHeads;  // multiple of 8
@@ -58,49 +78,59 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const bf16* __restrict__ 
   const int qb = lin % nqb;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lh = lane >> 5;
   const int hoff = head * kHeadDim;
 
-  // Q^T fragments (B operand): lane holds query row lr, dims 16 s + 8 lh .. +8.
-  const int qrow = min(qb * kBQ + wave * 32 + lr, n - 1);
-  bf16x8 qf[8];
+  // Q of this wave's 32 rows goes to LDS once (same layout as a K tile, 16
+  // rows per 4 KiB... 32 rows = 8 KiB per wave); the Q^T fragments (B
+  // operand: query row lr, dims 16 s + 8 lh .. +8) are re-read per tile,
+  // which keeps them out of the register file.
+  {
+    const int sub = lane >> 4, pc = lane & 15;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) qf[s] = *(const bf16x8*)(q + (size_t)qrow * ldq + hoff + 16 * s + 8 * lh);
-
-  // Staging assignments.  K: chunk ids tid + 256 i -> (row, 16-byte chunk).
-  // V: thread covers keys 4 kg .. 4 kg + 3 and dims 8 dg .. 8 dg + 7.
-  const int kg = tid >> 4, dg = tid & 15;
-  bf16x8 rk[4], rv[4];
-  auto load_tile = [&](int key0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i;
-      const int row = min(key0 + (id >> 4), n - 1);
-      rk[i] = *(const bf16x8*)(k + (size_t)row * ldk + hoff + (id & 15) * 8);
+    for (int b = 0; b < 8; ++b) {
+      const int row = 4 * b + sub;  // 0..31 within the wave
+      const int grow = min(qb * kBQ + wave * 32 + row, n - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const gmem_void_t*)(q + (size_t)grow * ldq + hoff + (pc ^ (row & 15)) * 8),
+          (lds_void_t*)(&qs_lds[wave * 512 + b * 64]), 16, 0, 0);
     }
+  }
+  const bf16x8* qw = qs_lds + wave * 512;
+
+  // Tile loads: each wave fills 4 KiB of K and 4 KiB of V per tile, 1 KiB
+  // (4 key rows) per global_load_lds; lane t lands at row t/16, physical chunk
+  // t%16 and so fetches the logical chunk that maps there.
+  const int sub_row = lane >> 4, pchunk = lane & 15;
+  auto issue_tile = [&](int tile, int slot) {
+    const int key0 = min(tile, (n - 1) / kBKV) * kBKV;  // a tile past the end reloads the last one
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = min(key0 + 4 * kg + i, n - 1);
-      rv[i] = *(const bf16x8*)(v + (size_t)row * ldv + hoff + 8 * dg);
+    for (int b = 0; b < 4; ++b) {
+      const int row = (wave * 4 + b) * 4 + sub_row;   // 0..63
+      const int grow = min(key0 + row, n - 1);
+      const int kc = pchunk ^ (row & 15);
+      const int vc = pchunk ^ (4 * (row & 3));
+      __builtin_amdgcn_global_load_lds((const gmem_void_t*)(k + (size_t)grow * ldk + hoff + kc * 8),
+                                       (lds_void_t*)(&ks_lds[slot][(wave * 4 + b) * 64]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const gmem_void_t*)(v + (size_t)grow * ldv + hoff + vc * 8),
+                                       (lds_void_t*)(&vs_lds[slot][(wave * 4 + b) * 64]), 16, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
+  constexpr int kLoadsPerTile = 8;  // per wave
+
+  // S^T = K Q^T for one tile (two 32-key fragments, interleaved chains).
+  auto scores = [&](int slot, floatx16 (&s)[2]) {
+    const floatx16 zero = {};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id >> 4, c = id & 15;
-      ks_lds[buf][row * 16 + (c ^ k_swz(row))] = rk[i];
-    }
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 qf = qw[k_phys(lr, 2 * st + lh)];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = 8 * dg + j;
-      bf16x4 t;
-      t[0] = rv[0][j];
-      t[1] = rv[1][j];
-      t[2] = rv[2][j];
-      t[3] = rv[3][j];
-      vt_lds[buf][d * 16 + (kg ^ vt_swz(d))] = t;
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = ks_lds[slot][k_phys(kb * 32 + lr, 2 * st + lh)];
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf, st == 0 ? zero : s[kb], 0, 0, 0);
+      }
     }
   };
 
@@ -112,91 +142,117 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const bf16* __restrict__ 
   float m_run = -INFINITY;  // running max (scaled, base-2 domain) of row lr
   float l_run = 0.f;        // this lane's partial row sum
 
-  const int ntiles = (n + kBKV - 1) / kBKV;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int key0 = t * kBKV;
-    if (t + 1 < ntiles) load_tile(key0 + kBKV);
-
-    // S^T = K Q^T for keys key0 .. key0+63 (two 32-key fragments).
-    floatx16 sacc[2];
+  // Transpose-read geometry: within its 16-lane group (g = lane / 16, i =
+  // lane % 16) a lane supplies the address of key 4h + i/4 (+ 16 j, + 8 for
+  // the second half of the fragment) and head dims 32 db + 16 (g % 2) +
+  // 4 (i % 4) .. +3; it receives head dim 32 db + lane % 32 of keys
+  // 16 j + 4 h + {0..3} (+ 8), h = lane / 32.
+  // The key rows read are tr_key + 16 j (+ 8); adding 16 j or 8 keeps
+  // row & 3, so the swizzled address of every read is the j = 0 address of
+  // its head-dim block plus a constant.
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int tr_key = 4 * lh + (i16 >> 2);
+  const int tr_dim = 16 * (g16 & 1) + 4 * (i16 & 3);  // + 32 db
+  int tr_off[4];                                        // bf16 element offsets, j = 0
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+  for (int db = 0; db < 4; ++db) {
+    const int dim = 32 * db + tr_dim;
+    tr_off[db] = v_phys(tr_key, dim >> 3) * 8 + (dim & 7);
+  }
+  auto pv = [&](int slot, const bf16x8 (&pf)[4]) {
+    const bf16* base = (const bf16*)vs_lds[slot];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-      const int row = kb * 32 + lr;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 a = ks_lds[buf][row * 16 + ((2 * s + lh) ^ k_swz(row))];
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+      for (int db = 0; db < 4; ++db) {
+        const bf16* p = base + tr_off[db] + 16 * j * kHeadDim;
+        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(p));
+        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(p + 8 * kHeadDim));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[j], oacc[db], 0, 0, 0);
       }
-    }
-    // Keys past the end of the sequence get probability 0.
-    if (key0 + kBKV > n) {
+  };
+
+  // Softmax of one tile: returns the probabilities as bf16 B operands and
+  // updates m_run / l_run / oacc.
+  auto softmax = [&](floatx16 (&s)[2], int key0, bf16x8 (&pf)[4]) {
+    if (key0 + kBKV > n) {  // keys past the end get probability 0
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          if (key >= n) sacc[kb][r] = -INFINITY;
+          if (key >= n) s[kb][r] = -INFINITY;
         }
     }
-    float mx = sacc[0][0];
+    float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = half_max(mx) * scale_log2;
+    // The reference max may lag the true running max by up to kSlack (base 2),
+    // so probabilities stay <= 2^kSlack; O and l share the reference, so the
+    // result is unchanged while the rescale (a wave-wide 64-register update)
+    // is only needed when some row's max jumps by more than that.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+    }
     float psum = 0.f;
-    bf16x8 pf[4];  // B operand per 16-key step j: keys of fragment j/2, registers 8 (j%2) ..
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], scale_log2, -m_new));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -m_run));
         psum += p;
         pf[kb * 2 + (r >> 3)][r & 7] = to_bf16(p);
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+    l_run += psum;
+  };
 
-    // O^T += V^T P^T.  Step j covers keys 16 j .. 16 j + 15; lane half lh
-    // supplies keys 16 j + {0..3, 8..11} + 4 lh, read from V^T as two 8-byte
-    // chunks (16 j + 4 lh) / 4 and (16 j + 8 + 4 lh) / 4.
+  const int ntiles = (n + kBKV - 1) / kBKV;
+  // Prologue: tiles 0..3 in flight, wait for 0 and 1, scores of tile 0.
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int d = db * 32 + lr;
-      const int sw = vt_swz(d);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x4 lo = vt_lds[buf][d * 16 + ((4 * j + lh) ^ sw)];
-        const bf16x4 hi = vt_lds[buf][d * 16 + ((4 * j + 2 + lh) ^ sw)];
-        bf16x8 a;
-        a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
-        a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[j], oacc[db], 0, 0, 0);
-      }
-    }
+  for (int t = 0; t < kNBuf; ++t) issue_tile(t, t);
+  wait_vmcnt<2 * kLoadsPerTile>();
+  __syncthreads();
+  floatx16 sa[2], sb[2];
+  bf16x8 pf[4];
+  scores(0, sa);
 
-    // Buffer buf ^ 1 was last read in the previous iteration, before its
-    // closing barrier, so it can be refilled now; the barrier below publishes it.
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+  // One iteration: scores of tile t+1 into `nxt` while the softmax of tile t
+  // (in `cur`) runs, then P V of tile t, then the ring advances.
+  // Every step is unconditional (straight-line loop body): a tile index past
+  // the end reloads the last tile, and a step on such a tile masks all of its
+  // keys, so it adds nothing.  Steps come in pairs (the score buffers swap
+  // roles), so an odd tile count runs one fully masked step.
+  auto step = [&](int t, floatx16 (&cur)[2], floatx16 (&nxt)[2]) {
+    scores((t + 1) % kNBuf, nxt);
+    softmax(cur, t * kBKV, pf);
+    pv(t % kNBuf, pf);
+    // Tile t+2 landed (only tile t+3 may still be in flight); after the
+    // barrier every wave is done with slot t % 4, which takes tile t+4.
+    wait_vmcnt<kLoadsPerTile>();
     __syncthreads();
+    issue_tile(t + kNBuf, t % kNBuf);
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, sa, sb);
+    step(t + 1, sb, sa);
   }
+  wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
 
   // Normalise and store: lane holds query row lr, dims db*32 + 8 g + 4 lh + 0..3.
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l_tot;
+  const float inv = 1.0f / half_sum(l_run);
   const int orow = qb * kBQ + wave * 32 + lr;
   if (orow < n) {
     bf16* op = o + (size_t)orow * ldo + hoff;
