@@ -8,10 +8,13 @@ sampler update x += (sigma_{k+1} - sigma_k) v.  Weights are seeded random init
 (N(0, 0.02) bf16, ~5.5 B parameters), inputs seeded N(0, 1) bf16.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --only KERNEL [--steps K]     # one kernel, for counter runs
 
 Prints one JSON line.  `value` is TFLOP/s of algorithmic work per step; the
-dominant kernel's roofline is measured live with HIP events on the stream
-the kernels run on.
+dominant kernel's roofline is measured live with HIP events on the stream the
+kernels run on.  --only runs a single kernel of the joint block at 4608 tokens
+(or the copy used to calibrate the HBM byte counters) K times and prints its
+average time.
 """
 from __future__ import annotations
 
@@ -25,6 +28,31 @@ HIDDEN, MLP = 3072, 9216
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "DiT step latency (ms) & TFLOP/s at 1024² (4608 tok); % of MI355X bf16 peak"
+COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
+
+# HBM bytes per launch at 4608 rows from rocprofv3 FETCH_SIZE + WRITE_SIZE
+# (calibrated against the 1 GiB copy: factors 2.0 and 1.0), with the sources
+# they were measured on; reported only while those sources are unchanged.
+TRAFFIC = {
+    "gemm_in_proj_swiglu": (1362.3e6 + 205.8e6, {"gemm_kernels.hpp": "aa3570c901eb1a96",
+                                                 "gemm.hip": "28b29a24a97a1b5f"}),
+    "gemm_out_proj_gated": (986.8e6 + 64.2e6, {"gemm_kernels.hpp": "aa3570c901eb1a96",
+                                               "gemm.hip": "28b29a24a97a1b5f"}),
+    "attention": (130.9e6 + 53.2e6, {"attention.hip": "4b249f5f06bd7f22"}),
+}
+
+
+def measured_traffic(kernel: str):
+    import hashlib
+    if kernel not in TRAFFIC:
+        return None
+    nbytes, sources = TRAFFIC[kernel]
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "latent_flow_matching_flux3_amd", "csrc")
+    for name, digest in sources.items():
+        with open(os.path.join(csrc, name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest()[:16] != digest:
+                return None
+    return nbytes
 
 
 def block_flops(n: int) -> float:
@@ -50,32 +78,68 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="in_proj | out_proj | attention | ln_modulate | qk_norm_rope | copy")
     ap.add_argument("--seed", type=int, default=0)
     return ap.parse_args()
 
 
-def build_model(L, torch, seed: int, n_early: int = 5, n_single: int = 28):
-    """Seeded random-init weights generated on the device, blocks packed."""
+def make_block(L, torch, rnd):
+    import flux3_synth as syn
+    w = {k: rnd(shp) for k, shp in syn.BLOCK_SHAPES.items() if not k.endswith("scale")}
+    w["norm.query_norm.scale"] = torch.ones(128, dtype=torch.bfloat16, device="cuda")
+    w["norm.key_norm.scale"] = torch.ones(128, dtype=torch.bfloat16, device="cuda")
+    b = L.PackedBlock(w)
+    torch.cuda.synchronize()
+    return b
+
+
+def device_rnd(torch, seed: int):
     import flux3_synth as syn
     g = torch.Generator(device="cuda").manual_seed(seed)
 
     def rnd(shape):
         t = torch.randn(*shape, generator=g, device="cuda", dtype=torch.float32).mul_(syn.WEIGHT_STD)
         return t.to(torch.bfloat16)
+    return rnd
 
+
+def build_model(L, torch, seed: int, n_early: int = 5, n_single: int = 28):
+    """Seeded random-init weights generated on the device, blocks packed."""
+    import flux3_synth as syn
+    rnd = device_rnd(torch, seed)
     glob = {k: rnd(shp) for k, shp in syn.GLOBAL_SHAPES.items()}
-
-    def block():
-        w = {k: rnd(shp) for k, shp in syn.BLOCK_SHAPES.items() if not k.endswith("scale")}
-        w["norm.query_norm.scale"] = torch.ones(128, dtype=torch.bfloat16, device="cuda")
-        w["norm.key_norm.scale"] = torch.ones(128, dtype=torch.bfloat16, device="cuda")
-        b = L.PackedBlock(w)
-        torch.cuda.synchronize()
-        return b
-
-    early = {m: [block() for _ in range(n_early)] for m in syn.MODES}
-    single = [block() for _ in range(n_single)]
+    early = {m: [make_block(L, torch, rnd) for _ in range(n_early)] for m in syn.MODES}
+    single = [make_block(L, torch, rnd) for _ in range(n_single)]
     return L.ModelWeights(glob, early, single)
+
+
+def kernel_fixtures(L, torch, blk, table, n_img: int, n: int):
+    """The joint block's kernels at n rows, each as (call, work, unit):
+    work is algorithmic FLOP (unit 'flop') or HBM bytes (unit 'byte') per call."""
+    g = torch.Generator(device="cuda").manual_seed(1)
+    xm = torch.empty((n, HIDDEN), dtype=torch.bfloat16, device="cuda")
+    qkv = torch.randn((n, 3 * HIDDEN), device="cuda", generator=g).to(torch.bfloat16)
+    cat = torch.randn((n, HIDDEN + MLP), device="cuda", generator=g).to(torch.bfloat16)
+    xs = torch.randn((n, HIDDEN), device="cuda", generator=g)
+    mod = torch.randn((2, 3, HIDDEN), device="cuda", generator=g) * 0.1
+    segs = [0, n_img, n]
+    L.flux3_ln_modulate(xs, xm, segs, mod)
+    qn = qkv.clone()
+    return {
+        "ln_modulate": (lambda: L.flux3_ln_modulate(xs, xm, segs, mod),
+                        6.0 * n * HIDDEN, "byte"),        # fp32 x in, bf16 out
+        "gemm_in_proj_swiglu": (lambda: L.flux3_block_in_proj(xm, blk.w_in, qkv, cat[:, HIDDEN:]),
+                                2.0 * n * HIDDEN * (3 * HIDDEN + 2 * MLP), "flop"),
+        "qk_norm_rope": (lambda: L.flux3_qk_norm_rope(qn[:, :HIDDEN], qn[:, HIDDEN:2 * HIDDEN],
+                                                      blk.q_scale, blk.k_scale, table),
+                         8.0 * n * HIDDEN + 512.0 * n, "byte"),  # q, k in and out + rope table
+        "attention": (lambda: L.flux3_attention(qkv[:, :HIDDEN], qkv[:, HIDDEN:2 * HIDDEN],
+                                                qkv[:, 2 * HIDDEN:], cat[:, :HIDDEN]),
+                      4.0 * n * n * HIDDEN, "flop"),
+        "gemm_out_proj_gated": (lambda: L.flux3_block_out_proj(cat, blk.w_out, xs, segs, mod),
+                                2.0 * n * (HIDDEN + MLP) * HIDDEN, "flop"),
+    }
 
 
 def event_time_ms(torch, fn, reps: int) -> float:
@@ -94,7 +158,6 @@ def event_time_ms(torch, fn, reps: int) -> float:
 def cpu_baseline(seed: int):
     """The CPU oracle (float64 NumPy), untuned, on a bounded sample: one joint
     block at 4608 tokens (image 64x64 + 512 text), two modulation segments."""
-    import numpy as np
     import torch
     import flux3_synth as syn
     import oracle as O
@@ -118,6 +181,29 @@ def cpu_baseline(seed: int):
                       f"{dt:.2f} s; the full step is {stack_flops(4096, 0, 512) / 1e12:.1f} TFLOP"}
 
 
+def run_only(args, L, torch, syn):
+    """One kernel, args.steps times, for counter collection."""
+    lay = syn.WORKLOADS["stack_t2i_1024_4608tok"]
+    n = lay.n_total
+    if args.only == "copy":
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        fn, work, unit = (lambda: torch.mul(src, 1.0, out=dst)), 2.0 * COPY_BYTES, "byte"
+    else:
+        blk = make_block(L, torch, device_rnd(torch, args.seed))
+        ids = L.flux3_build_ids(lay.img_h, lay.img_w, lay.n_txt).to("cuda")
+        table = L.flux3_rope_table(ids)
+        names = {"in_proj": "gemm_in_proj_swiglu", "out_proj": "gemm_out_proj_gated"}
+        fx = kernel_fixtures(L, torch, blk, table, lay.n_img, n)
+        fn, work, unit = fx[names.get(args.only, args.only)]
+    ms = event_time_ms(torch, fn, args.steps)
+    rate = work / (ms * 1e-3) / (1e12 if unit == "flop" else 1e9)
+    print(json.dumps({"kernel": args.only, "calls": args.steps + 1, "ms": round(ms, 4),
+                      "work_per_call": work, "rate": round(rate, 1),
+                      "rate_unit": "TFLOP/s" if unit == "flop" else "GB/s"}), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -130,11 +216,13 @@ def main():
 
     assert torch.cuda.is_available(), "no GPU visible"
     L.lib()
+    if args.only:
+        return run_only(args, L, torch, syn)
     lay = syn.WORKLOADS["stack_t2i_1024_4608tok"]
     n_img, n_txt = lay.n_img, lay.n_txt
     n = n_img + n_txt
 
-    print(f"[bench] building ~5.5B-parameter model on the device", file=sys.stderr, flush=True)
+    print("[bench] building ~5.5B-parameter model on the device", file=sys.stderr, flush=True)
     model = build_model(L, torch, args.seed)
     img = syn.latents(args.seed + 1, n_img).to("cuda")
     txt = syn.text_features(args.seed + 2, n_txt).to("cuda")
@@ -173,50 +261,29 @@ def main():
 
     # Per-kernel timing at the joint-block shape (4608 rows), same stream.
     print("[bench] per-kernel timing", file=sys.stderr, flush=True)
-    blk = model.single[0]
-    xm = torch.empty((n, HIDDEN), dtype=torch.bfloat16, device="cuda")
-    qkv = torch.empty((n, 3 * HIDDEN), dtype=torch.bfloat16, device="cuda")
-    cat = torch.empty((n, HIDDEN + MLP), dtype=torch.bfloat16, device="cuda")
-    xs = torch.randn((n, HIDDEN), device="cuda")
-    mod = torch.randn((2, 3, HIDDEN), device="cuda") * 0.1
-    segs = [0, n_img, n]
-    L.flux3_ln_modulate(xs, xm, segs, mod)
-    reps = args.kernel_reps
-    kern = {}
-    kern["ln_modulate"] = event_time_ms(torch, lambda: L.flux3_ln_modulate(xs, xm, segs, mod), reps)
-    kern["gemm_in_proj_swiglu"] = event_time_ms(
-        torch, lambda: L.flux3_block_in_proj(xm, blk.w_in, qkv, cat[:, HIDDEN:]), reps)
-    qn = qkv.clone()
-    kern["qk_norm_rope"] = event_time_ms(
-        torch, lambda: L.flux3_qk_norm_rope(qn[:, :HIDDEN], qn[:, HIDDEN:2 * HIDDEN], blk.q_scale, blk.k_scale,
-                                            table), reps)
-    kern["attention"] = event_time_ms(
-        torch, lambda: L.flux3_attention(qkv[:, :HIDDEN], qkv[:, HIDDEN:2 * HIDDEN], qkv[:, 2 * HIDDEN:],
-                                         cat[:, :HIDDEN]), reps)
-    kern["gemm_out_proj_gated"] = event_time_ms(
-        torch, lambda: L.flux3_block_out_proj(cat, blk.w_out, xs, segs, mod), reps)
+    fx = kernel_fixtures(L, torch, model.single[0], table, n_img, n)
+    per_kernel = {}
+    for name, (fn, work, unit) in fx.items():
+        kms = event_time_ms(torch, fn, args.kernel_reps)
+        if unit == "flop":
+            per_kernel[name] = {"ms": round(kms, 4), "tflops": round(work / kms / 1e9, 1)}
+        else:
+            per_kernel[name] = {"ms": round(kms, 4), "gbs": round(work / kms / 1e6, 1)}
     torch.cuda.synchronize()
-
-    in_flops = 2.0 * n * HIDDEN * (3 * HIDDEN + 2 * MLP)
-    out_flops = 2.0 * n * (HIDDEN + MLP) * HIDDEN
-    att_flops = 4.0 * n * n * HIDDEN
-    share = {"gemm_in_proj_swiglu": kern["gemm_in_proj_swiglu"], "attention": kern["attention"],
-             "gemm_out_proj_gated": kern["gemm_out_proj_gated"]}
-    dom = max(share, key=share.get)
-    dom_flops = {"gemm_in_proj_swiglu": in_flops, "attention": att_flops, "gemm_out_proj_gated": out_flops}[dom]
-    achieved = dom_flops / (kern[dom] * 1e-3) / 1e12
-    per_kernel = {
-        "gemm_in_proj_swiglu": {"ms": kern["gemm_in_proj_swiglu"],
-                                "tflops": in_flops / kern["gemm_in_proj_swiglu"] / 1e9},
-        "attention": {"ms": kern["attention"], "tflops": att_flops / kern["attention"] / 1e9},
-        "gemm_out_proj_gated": {"ms": kern["gemm_out_proj_gated"],
-                                "tflops": out_flops / kern["gemm_out_proj_gated"] / 1e9},
-        # algorithmic bytes: LN reads x and writes xm (bf16) = 4 N H
-        "ln_modulate": {"ms": kern["ln_modulate"], "gbs": 4.0 * n * HIDDEN / kern["ln_modulate"] / 1e6},
-        # q and k read and written (bf16) + the rope table (512 B per token)
-        "qk_norm_rope": {"ms": kern["qk_norm_rope"],
-                         "gbs": (8.0 * n * HIDDEN + 512.0 * n) / kern["qk_norm_rope"] / 1e6},
-    }
+    # Dominant kernel: most time per step.  The joint blocks dominate (28 of
+    # 38 block calls, at the largest row count); each block calls every
+    # kernel once, so the longest kernel is the dominant one.
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["ms"])
+    dom_work, dom_unit = fx[dom][1], fx[dom][2]
+    if dom_unit == "flop":
+        achieved = dom_work / (per_kernel[dom]["ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom)}
+    else:
+        achieved = dom_work / (per_kernel[dom]["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -234,6 +301,7 @@ def main():
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 3),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "steps_per_s": round(1e3 / ms, 3),
+        "image_s_16_steps": round(16 * ms / 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -242,8 +310,7 @@ def main():
         "config": {"workload": "stack_t2i_1024_4608tok", "image_tokens": n_img, "text_tokens": n_txt,
                    "blocks": "5 per-stream + 28 joint", "params": "5.55B", "tflop_per_step": round(flops / 1e12, 3),
                    "sampler": "flow map, 16-step shifted schedule (alpha 6.93)", "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "roofline": roof,
         "kernels": per_kernel,
         "cpu_baseline": cpu,
     }
