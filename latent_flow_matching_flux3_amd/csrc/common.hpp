@@ -59,6 +59,8 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// silu(x) = x / (1 + e^-x) with the hardware reciprocal (1 ulp); -0 for
+// x -> -inf, x for x -> +inf.
+__device__ __forceinline__ float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 }  // namespace flux3

@@ -10,6 +10,8 @@
 // The kernels themselves are in gemm_kernels.hpp.
 #include "gemm_kernels.hpp"
 
+#include <algorithm>
+
 namespace flux3 {
 
 namespace {
@@ -22,24 +24,59 @@ void run_regs(const GemmArgs& g, hipStream_t st) {
                      dim3(WM * WN * 64), 0, st, g, tiles_m, tiles_n);
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int ST, int WPE>
-void run_ring(const GemmArgs& g, hipStream_t st) {
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Persistent launch: one workgroup per CU (WPE workgroups per CU when the
+// ring leaves room), never more workgroups than tiles; one kernel per
+// epilogue kind.
+template <int BM, int BN, int WM, int WN, int BK, int ST, int WPE, GemmEpi EPI>
+void launch_ring(const GemmArgs& g, hipStream_t st) {
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = g.N / BN;
-  hipLaunchKernelGGL((gemm::gemm_ring_kernel<BM, BN, WM, WN, BK, ST, WPE>), dim3(tiles_m * tiles_n),
+  const int total = tiles_m * tiles_n;
+  const int grid = std::min(total, cu_count() * WPE);
+  hipLaunchKernelGGL((gemm::gemm_ring_kernel<BM, BN, WM, WN, BK, ST, WPE, EPI>), dim3(grid),
                      dim3(WM * WN * 64), 0, st, g, tiles_m, tiles_n);
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int ST, int WPE>
+void run_ring(const GemmArgs& g, hipStream_t st) {
+  switch (g.epi) {
+    case GemmEpi::kStoreBf16: launch_ring<BM, BN, WM, WN, BK, ST, WPE, GemmEpi::kStoreBf16>(g, st); break;
+    case GemmEpi::kStoreF32: launch_ring<BM, BN, WM, WN, BK, ST, WPE, GemmEpi::kStoreF32>(g, st); break;
+    case GemmEpi::kInProj: launch_ring<BM, BN, WM, WN, BK, ST, WPE, GemmEpi::kInProj>(g, st); break;
+    case GemmEpi::kGatedResidual: launch_ring<BM, BN, WM, WN, BK, ST, WPE, GemmEpi::kGatedResidual>(g, st); break;
+  }
 }
 
 }  // namespace
 
-// Tile choice: 256x256 (8 waves, 128x64 per wave) when the grid still has at
-// least one tile per CU; otherwise 128x128 (4 waves, 64x64 per wave); 64-wide
-// outputs use 64x64 tiles.  The host has checked K % 64 == 0 and N % 64 == 0.
+// Tile choice: 256x256 tiles on the persistent ring kernel (4 waves, 128x128
+// per wave) when there are at least 192 of them; otherwise the register-staged
+// kernel with 128x128 tiles (4 waves, 64x64 per wave), or 64x64 tiles for
+// outputs whose width is not a multiple of 128.  The host has checked
+// K % 64 == 0 and N % 64 == 0.
 void launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 0) return;
   const long big_tiles = (long)((g.M + 255) / 256) * (g.N / 256);
   if (g.N % 256 == 0 && big_tiles >= 192) {
-    run_ring<256, 256, 2, 2, 64, 2, 1>(g, st);
+    // Long products (the block's output projection, K = 12288) keep more
+    // slices in flight: five 32-wide slices instead of two 64-wide ones.
+    if (g.K >= 8192)
+      run_ring<256, 256, 2, 2, 32, 5, 1>(g, st);
+    else
+      run_ring<256, 256, 2, 2, 64, 2, 1>(g, st);
   } else if (g.N % 128 == 0) {
     run_regs<128, 128, 2, 2>(g, st);
   } else {
@@ -52,17 +89,10 @@ int launch_gemm_variant(const GemmArgs& g, int cfg, hipStream_t st) {
   switch (cfg) {
     case 0: run_regs<256, 256, 2, 4>(g, st); return 0;
     case 1: run_regs<128, 128, 2, 2>(g, st); return 0;
-    case 2: run_ring<256, 256, 2, 2, 32, 4, 1>(g, st); return 0;
-    case 3: run_ring<256, 256, 2, 2, 32, 3, 1>(g, st); return 0;
-    case 4: run_ring<128, 256, 2, 2, 32, 3, 2>(g, st); return 0;
-    case 5: run_ring<256, 128, 2, 2, 32, 3, 2>(g, st); return 0;
-    case 6: run_ring<128, 128, 2, 2, 32, 4, 2>(g, st); return 0;
-    case 7: run_ring<256, 128, 2, 2, 64, 3, 1>(g, st); return 0;
-    case 8: run_ring<128, 256, 2, 2, 64, 3, 1>(g, st); return 0;
     case 9: run_ring<256, 256, 2, 2, 64, 2, 1>(g, st); return 0;
-    case 10: run_ring<256, 128, 2, 2, 64, 2, 2>(g, st); return 0;
-    default: return -1;
+    case 11: run_ring<256, 256, 2, 2, 32, 5, 1>(g, st); return 0;
   }
+  return -1;
 }
 
 }  // namespace flux3

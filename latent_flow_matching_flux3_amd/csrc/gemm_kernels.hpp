@@ -27,6 +27,9 @@ namespace gemm {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gmem_void_t;
 
+
+
+
 // Rows of a K slice of width BK hold CPR = BK/8 chunks of 16 bytes; RPL rows
 // share a 256-byte bank line.  Chunk c of row r lives at c ^ swz(r).
 template <int BK>
@@ -62,10 +65,9 @@ struct Tile {
 // Tile order: XCD-contiguous bands of the tile grid (workgroups are dealt to
 // the 8 XCDs round-robin), then groups of 4 tile rows, so the tiles running
 // at the same time on one XCD share A rows and B rows in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
-  int lin = blockIdx.x;
-  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+// Position `lin` of the grouped order: groups of 4 tile rows, walked column
+// by column, so neighbouring positions share A rows or B rows.
+__device__ __forceinline__ void grouped_coords(int lin, int tiles_m, int tiles_n, int& tm, int& tn) {
   constexpr int GM = 4;
   const int group = lin / (GM * tiles_n);
   const int first_m = group * GM;
@@ -75,100 +77,166 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = in_group / gsize;
 }
 
-template <class T>
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  int lin = blockIdx.x;
+  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  grouped_coords(lin, tiles_m, tiles_n, tm, tn);
+}
+
+// Tiles of one workgroup of a persistent launch (gridDim.x workgroups, at
+// most one per CU, all resident).  Workgroup b runs on XCD b % 8; XCD x owns
+// a contiguous band of the grouped order, sized to its workgroup count so
+// every workgroup gets floor or ceil of tiles / gridDim.x tiles, and its
+// workgroups take the band's tiles round-robin: the tiles one XCD runs at
+// the same time are neighbours and share operand rows in its L2.
+struct TileWalk {
+  int lo, first, step, count;
+  __device__ __forceinline__ TileWalk(int total) {
+    const int G = gridDim.x, b = blockIdx.x, x = b & 7;
+    const int q = total / G, r = total % G;
+    lo = 0;
+    int cnt = 0;
+#pragma unroll
+    for (int y = 0; y < 8; ++y) {
+      const int c = q * ((G - y + 7) >> 3) + (r > y ? (r - y + 7) >> 3 : 0);
+      if (y < x) lo += c;
+      if (y == x) cnt = c;
+    }
+    step = (G - x + 7) >> 3;
+    first = b >> 3;
+    count = first < cnt ? (cnt - first + step - 1) / step : 0;
+  }
+  __device__ __forceinline__ void coords(int i, int tiles_m, int tiles_n, int& tm, int& tn) const {
+    grouped_coords(lo + first + i * step, tiles_m, tiles_n, tm, tn);
+  }
+};
+
+// Epilogue of one wave's WTM x WTN accumulator tile (rows wrow0.., columns
+// wcol0..), for one epilogue kind.  Each lane owns one output row and 4
+// consecutive columns per group of 4 accumulator registers.
+//
+// Register discipline: a spilled register reloaded here would wait for every
+// store issued before it (vmcnt counts stores on this architecture).  The
+// lane index is recomputed here by an opaque instruction pair, so no per-lane
+// address arithmetic is hoisted into the surrounding tile loop to hold a
+// register there, and scheduling fences after each fragment keep the
+// accumulator reads of one fragment together.
+template <class T, GemmEpi EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::FM][T::FN],
-                                         int wrow0, int wcol0, int lane) {
+                                         int wrow0, int wcol0) {
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
   const int lr = lane & 31;
-  switch (g.epi) {
-    case GemmEpi::kStoreBf16:
-    case GemmEpi::kInProj: {
-      if (g.epi == GemmEpi::kStoreBf16 || wcol0 < 3 * kHidden) {
-        bf16* C = (bf16*)g.C;
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i) {
-          const int row = wrow0 + 32 * i + lr;
-          if (row < g.M) {
-            bf16* crow = C + (size_t)row * g.ldc + wcol0;
-#pragma unroll
-            for (int j = 0; j < T::FN; ++j)
-#pragma unroll
-              for (int g4 = 0; g4 < 4; ++g4) {
-                bf16x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = to_bf16(acc[i][j][4 * g4 + e]);
-                *(bf16x4*)(crow + 32 * j + frag_col(g4, lane)) = v;
-              }
-          }
-        }
-      } else {
-        // SwiGLU: fragment 2p holds a-columns, 2p+1 the matching b-columns.
-        static_assert(T::FN % 2 == 0, "SwiGLU needs fragment pairs");
-        const int hcol0 = (wcol0 - 3 * kHidden) / 2;
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i) {
-          const int row = wrow0 + 32 * i + lr;
-          if (row < g.M) {
-            bf16* hrow = g.H + (size_t)row * g.ldh + hcol0;
-#pragma unroll
-            for (int p = 0; p < T::FN / 2; ++p)
-#pragma unroll
-              for (int g4 = 0; g4 < 4; ++g4) {
-                bf16x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const float a = acc[i][2 * p][4 * g4 + e], b = acc[i][2 * p + 1][4 * g4 + e];
-                  v[e] = to_bf16(silu_f(a) * b);
-                }
-                *(bf16x4*)(hrow + 32 * p + frag_col(g4, lane)) = v;
-              }
-          }
-        }
-      }
-      break;
-    }
-    case GemmEpi::kStoreF32: {
-      float* C = (float*)g.C;
+  if constexpr (EPI == GemmEpi::kStoreBf16 || EPI == GemmEpi::kInProj) {
+    if (EPI == GemmEpi::kStoreBf16 || wcol0 < 3 * kHidden) {
+      bf16* C = (bf16*)g.C;
 #pragma unroll
       for (int i = 0; i < T::FM; ++i) {
         const int row = wrow0 + 32 * i + lr;
         if (row < g.M) {
-          float* crow = C + (size_t)row * g.ldc + wcol0;
+          bf16* crow = C + (size_t)row * g.ldc + wcol0;
 #pragma unroll
-          for (int j = 0; j < T::FN; ++j)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4)
-              *(float4*)(crow + 32 * j + frag_col(g4, lane)) =
-                  make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
-                              acc[i][j][4 * g4 + 3]);
-        }
-      }
-      break;
-    }
-    case GemmEpi::kGatedResidual: {
-      float* X = (float*)g.C;
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i) {
-        const int row = wrow0 + 32 * i + lr;
-        if (row < g.M) {
-          const float* gate = g.mod + (size_t)seg_of_row(g.seg, row) * g.mod_stride + g.gate_offset + wcol0;
-          float* xrow = X + (size_t)row * g.ldc + wcol0;
-#pragma unroll
-          for (int j = 0; j < T::FN; ++j)
+          for (int j = 0; j < T::FN; ++j) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-              const int c = 32 * j + frag_col(g4, lane);
-              const float4 gt = *(const float4*)(gate + c);
-              float4 xv = *(const float4*)(xrow + c);
-              xv.x += gt.x * acc[i][j][4 * g4];
-              xv.y += gt.y * acc[i][j][4 * g4 + 1];
-              xv.z += gt.z * acc[i][j][4 * g4 + 2];
-              xv.w += gt.w * acc[i][j][4 * g4 + 3];
-              *(float4*)(xrow + c) = xv;
+              bf16x4 v;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = to_bf16(acc[i][j][4 * g4 + e]);
+              *(bf16x4*)(crow + 32 * j + frag_col(g4, lane)) = v;
             }
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
-      break;
+    } else {
+      // SwiGLU: fragment 2p holds a-columns, 2p+1 the matching b-columns.
+      static_assert(T::FN % 2 == 0, "SwiGLU needs fragment pairs");
+      const int hcol0 = (wcol0 - 3 * kHidden) / 2;
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) {
+        const int row = wrow0 + 32 * i + lr;
+        if (row < g.M) {
+          bf16* hrow = g.H + (size_t)row * g.ldh + hcol0;
+#pragma unroll
+          for (int p = 0; p < T::FN / 2; ++p) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              bf16x4 v;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float a = acc[i][2 * p][4 * g4 + e], b = acc[i][2 * p + 1][4 * g4 + e];
+                v[e] = to_bf16(silu_f(a) * b);
+              }
+              *(bf16x4*)(hrow + 32 * p + frag_col(g4, lane)) = v;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
     }
+  } else if constexpr (EPI == GemmEpi::kStoreF32) {
+    float* C = (float*)g.C;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      const int row = wrow0 + 32 * i + lr;
+      if (row < g.M) {
+        float* crow = C + (size_t)row * g.ldc + wcol0;
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *(float4*)(crow + 32 * j + frag_col(g4, lane)) =
+                make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                            acc[i][j][4 * g4 + 3]);
+      }
+    }
+  } else {
+    static_assert(EPI == GemmEpi::kGatedResidual, "epilogue kind");
+    // x and gate are distinct buffers: all loads of one fragment are issued
+    // before its stores.
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      const int row = wrow0 + 32 * i + lr;
+      if (row < g.M) {
+        const float* __restrict__ gate =
+            g.mod + (size_t)seg_of_row(g.seg, row) * g.mod_stride + g.gate_offset + wcol0;
+        float* __restrict__ xrow = (float*)g.C + (size_t)row * g.ldc + wcol0;
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+          float4 gt[4], xv[4];
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int c = 32 * j + frag_col(g4, lane);
+            gt[g4] = *(const float4*)(gate + c);
+            xv[g4] = *(const float4*)(xrow + c);
+          }
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int c = 32 * j + frag_col(g4, lane);
+            float4 r = xv[g4];
+            r.x += gt[g4].x * acc[i][j][4 * g4];
+            r.y += gt[g4].y * acc[i][j][4 * g4 + 1];
+            r.z += gt[g4].z * acc[i][j][4 * g4 + 2];
+            r.w += gt[g4].w * acc[i][j][4 * g4 + 3];
+            *(float4*)(xrow + c) = r;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
+}
+
+// Runtime-selected epilogue (small-shape kernel).
+template <class T>
+__device__ __forceinline__ void epilogue_any(const GemmArgs& g, floatx16 (&acc)[T::FM][T::FN],
+                                             int wrow0, int wcol0) {
+  switch (g.epi) {
+    case GemmEpi::kStoreBf16: epilogue<T, GemmEpi::kStoreBf16>(g, acc, wrow0, wcol0); break;
+    case GemmEpi::kStoreF32: epilogue<T, GemmEpi::kStoreF32>(g, acc, wrow0, wcol0); break;
+    case GemmEpi::kInProj: epilogue<T, GemmEpi::kInProj>(g, acc, wrow0, wcol0); break;
+    case GemmEpi::kGatedResidual: epilogue<T, GemmEpi::kGatedResidual>(g, acc, wrow0, wcol0); break;
   }
 }
 
@@ -278,29 +346,32 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_regs_kernel(GemmArgs g, int 
     __syncthreads();
   }
 
-  epilogue<T>(g, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
+  epilogue_any<T>(g, acc, m0 + wm * T::WTM, n0 + wn * T::WTN);
 }
 
 // ---------------------------------------------------------------------------
-// Ring kernel.
+// Ring kernel (persistent).
 //
-// STAGES LDS buffers hold K slices of width BK; slice s lives in buffer
-// s % STAGES.  Each global_load_lds_dwordx4 of a wave fills one KiB of a
-// buffer (RPB rows); lane t lands at chunk t of that KiB (row t / CPR,
-// physical chunk t % CPR), so it fetches logical chunk (t % CPR) ^ swz(row).
+// STAGES LDS buffers hold K slices of width BK.  Each global_load_lds_dwordx4
+// of a wave fills one KiB of a buffer (RPB rows); lane t lands at chunk t of
+// that KiB (row t / CPR, physical chunk t % CPR), so it fetches logical chunk
+// (t % CPR) ^ swz(row).
 //
-// Per slice kt (KSTEPS = BK/16 MFMA steps of FM x FN MFMAs per wave):
+// A workgroup walks its tiles (TileWalk) and the K slices of consecutive
+// tiles form one stream through the ring: the first slices of the next tile
+// are loading while the current tile finishes, and its output stores drain
+// behind the next tile's MFMAs.
+//
+// Per slice (KSTEPS = BK/16 MFMA steps of FM x FN MFMAs per wave):
 //   steps 0 .. KSTEPS-2 : read the fragments of the next step, then the MFMAs
 //                         of this step (the reads hide behind the MFMAs);
-//   before the last step: wait until this wave's copy of slice kt+1 landed,
-//                         barrier (slice kt+1 visible to all; everyone has
-//                         read all of slice kt), read the first fragments of
-//                         slice kt+1, then the last MFMAs of slice kt with the
-//                         refill of buffer kt % STAGES (slice kt + STAGES)
-//                         issued one load per MFMA between them.
-// So the MFMA pipe only waits on the barrier itself; STAGES-2 slices are in
-// flight while a slice is consumed.
-// ---------------------------------------------------------------------------
+//   before the last step: wait until this wave's copy of the next slice
+//                         landed, barrier (next slice visible to all; everyone
+//                         has read all of this slice), read the first
+//                         fragments of the next slice, then the last MFMAs of
+//                         this slice with the refill of its buffer (the slice
+//                         STAGES ahead) issued one load per MFMA between them;
+//   after the last slice of a tile: the epilogue, then zero accumulators.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
@@ -308,22 +379,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Wait until at most n_after * PER loads of this wave are outstanding.
-template <int PER, int MAXN>
-__device__ __forceinline__ void wait_slices(int n_after) {
-  if constexpr (MAXN >= 3) {
-    if (n_after >= 3) { wait_vmcnt<3 * PER>(); return; }
-  }
-  if constexpr (MAXN >= 2) {
-    if (n_after == 2) { wait_vmcnt<2 * PER>(); return; }
-  }
-  if constexpr (MAXN >= 1) {
-    if (n_after == 1) { wait_vmcnt<PER>(); return; }
-  }
-  wait_vmcnt<0>();
-}
-
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WAVES_PER_EU>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WAVES_PER_EU, GemmEpi EPI>
 __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   using T = Tile<BM, BN, WM, WN>;
@@ -337,46 +393,86 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   constexpr int KSTEPS = BK / 16;
   constexpr int NMF = T::FM * T::FN;         // MFMAs per step
   static_assert(BM % (Lay::RPB * NW) == 0 && BN % (Lay::RPB * NW) == 0, "rows must split over waves");
-  static_assert((STAGES - 1) * PER < 64 && STAGES >= 2 && STAGES <= 4, "ring depth");
+  static_assert((STAGES - 1) * PER < 64 && STAGES >= 2 && STAGES <= 5, "ring depth");
   static_assert(KSTEPS >= 2, "BK >= 32");
   __shared__ bf16x8 lds[STAGES * STAGE];
+
+  const TileWalk walk(tiles_m * tiles_n);
+  if (walk.count == 0) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
 
-  // Source pointers of this lane for each of its PER loads (A rows clamped).
+  // Load addresses: a uniform tile base (scalar registers) plus a 32-bit
+  // per-lane byte offset.  A lane's offset inside a KiB block depends only on
+  // the block's parity (the swizzle) and, for A, on the clamp of rows past
+  // M-1 in the last tile row, so A keeps one offset per block and B one per
+  // parity.
+  static_assert(B_BLK % 2 == 0, "block parity fixed per B load");
   const int sub_row = lane / CPR;
-  const bf16* src[PER];
+  unsigned voff_a[A_BLK], voff_b[2];
 #pragma unroll
-  for (int i = 0; i < A_BLK; ++i) {
-    const int b = wave * A_BLK + i;
-    const int row = b * Lay::RPB + sub_row;
-    src[i] = g.A + (size_t)min(m0 + row, g.M - 1) * g.lda + ((lane % CPR) ^ Lay::swz(row)) * 8;
+  for (int p = 0; p < 2; ++p) {
+    const int chunk = (lane % CPR) ^ ((4 * p + sub_row / Lay::RPL) % CPR);
+    voff_b[p] = (unsigned)(sub_row * g.ldb * 2 + chunk * 16);
   }
+  const char* a_tile;
+  const char* b_tile;
+  auto set_src = [&](int i) {
+    int tm, tn;
+    walk.coords(i, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM;
+    a_tile = (const char*)(g.A + (size_t)m0 * g.lda);
+    b_tile = (const char*)(g.B + (size_t)tn * BN * g.ldb);
 #pragma unroll
-  for (int i = 0; i < B_BLK; ++i) {
-    const int b = wave * B_BLK + i;
-    const int row = b * Lay::RPB + sub_row;
-    src[A_BLK + i] = g.B + (size_t)(n0 + row) * g.ldb + ((lane % CPR) ^ Lay::swz(row)) * 8;
-  }
+    for (int q = 0; q < A_BLK; ++q) {
+      const int row = (wave * A_BLK + q) * Lay::RPB + sub_row;
+      const int chunk = (lane % CPR) ^ Lay::swz(row);
+      voff_a[q] = (unsigned)((min(m0 + row, g.M - 1) - m0) * g.lda * 2 + chunk * 16);
+    }
+  };
   auto load_one = [&](int q, int slot, int koff) {
-    const int blk = q < A_BLK ? wave * A_BLK + q : BM / Lay::RPB + wave * B_BLK + (q - A_BLK);
-    __builtin_amdgcn_global_load_lds((const gmem_void_t*)(src[q] + koff),
-                                     (lds_void_t*)(lds + slot * STAGE + blk * 64), 16, 0, 0);
+    if (q < A_BLK) {
+      const int blk = wave * A_BLK + q;
+      __builtin_amdgcn_global_load_lds((const gmem_void_t*)(a_tile + koff * 2 + voff_a[q]),
+                                       (lds_void_t*)(lds + slot * STAGE + blk * 64), 16, 0, 0);
+    } else {
+      const int blk = wave * B_BLK + (q - A_BLK);
+      __builtin_amdgcn_global_load_lds(
+          (const gmem_void_t*)(b_tile + ((size_t)blk * Lay::RPB * g.ldb + koff) * 2 + voff_b[q & 1]),
+          (lds_void_t*)(lds + slot * STAGE + (BM / Lay::RPB + blk) * 64), 16, 0, 0);
+    }
+  };
+  // Load cursor: tile ld_i, slice ld_kt.  Past the last slice it stays there:
+  // every refill still issues PER loads (the final slice again, into buffers
+  // that are no longer read), so the count of loads in flight behind a given
+  // slice is constant.
+  const int KT = g.K / BK;  // >= 1
+  int ld_i = 0, ld_kt = 0;
+  auto advance_load = [&]() {
+    if (++ld_kt == KT) {
+      if (ld_i + 1 < walk.count) {
+        ++ld_i;
+        ld_kt = 0;
+        set_src(ld_i);
+      } else {
+        ld_kt = KT - 1;
+      }
+    }
   };
 
   floatx16 acc[T::FM][T::FN];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int i = 0; i < T::FM; ++i)
+    for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < T::FN; ++j)
+      for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  };
+  zero_acc();
 
   const int lr = lane & 31, lh = lane >> 5;
   const int sw = Lay::swz(lr);  // rows read by this lane are 32 k + lr
@@ -413,16 +509,24 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // Output origin of this wave in the tile being computed, found before the
+  // tile's main loop (scalar registers), so nothing but the epilogue itself
+  // runs between the last MFMA and the stores.
+  int out_row = 0, out_col = 0;
+  auto set_out = [&](int i) {
+    int tm, tn;
+    walk.coords(i, tiles_m, tiles_n, tm, tn);
+    out_row = __builtin_amdgcn_readfirstlane(tm * BM + wm * T::WTM);
+    out_col = __builtin_amdgcn_readfirstlane(tn * BN + wn * T::WTN);
+  };
+  auto store_tile = [&]() { epilogue<T, EPI>(g, acc, out_row, out_col); };
 
-  const int KT = g.K / BK;  // >= 1
-  // Every iteration issues exactly PER loads (the last STAGES of them reload
-  // the final slice into buffers that are no longer read), so the number of
-  // loads in flight behind a given slice is constant.
-  auto slice_off = [&](int s) { return min(s, KT - 1) * BK; };
+  set_src(0);
 #pragma unroll
   for (int s = 0; s < STAGES; ++s) {
 #pragma unroll
-    for (int q = 0; q < PER; ++q) load_one(q, s, slice_off(s));
+    for (int q = 0; q < PER; ++q) load_one(q, s, ld_kt * BK);
+    advance_load();
   }
   wait_vmcnt<(STAGES - 1) * PER>();
   __syncthreads();
@@ -432,33 +536,43 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   read_frags(0, 0, 0);
 
   constexpr int pl = (KSTEPS - 1) & 1;  // fragment slot of the last step (1)
-  for (int kt = 0; kt + 1 < KT; ++kt) {
-    const int cur = (kt % STAGES) * STAGE;
-    inner_steps(cur);
-    // Slice kt+1 landed for this wave (STAGES-2 slices issued after it), and
-    // after the barrier for every wave; everyone has read all of slice kt.
-    wait_vmcnt<(STAGES - 2) * PER>();
-    __syncthreads();
-    read_frags(((kt + 1) % STAGES) * STAGE, 0, pl ^ 1);
-    const int koff = slice_off(kt + STAGES);
+  int slot = 0;
+  for (int ti = 0; ti < walk.count; ++ti) {
+    set_out(ti);
+    for (int kt = 0; kt < KT; ++kt) {
+      inner_steps(slot * STAGE);
+      // The next slice landed for this wave (STAGES-2 slices issued after
+      // it), and after the barrier for every wave; everyone has read this
+      // slice.
+      wait_vmcnt<(STAGES - 2) * PER>();
+      __syncthreads();
+      const int next = slot + 1 == STAGES ? 0 : slot + 1;
+      // At a tile end the next slice's first fragments are read after the
+      // epilogue, so they are not live across it.
+      if (kt + 1 < KT) read_frags(next * STAGE, 0, pl ^ 1);
+      const int koff = ld_kt * BK;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+          acc[i][j] = mma(af[pl][i], bfr[pl][j], acc[i][j]);
+#pragma unroll
+          for (int q = i * T::FN + j; q < PER; q += NMF) load_one(q, slot, koff);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      advance_load();
+      slot = next;
+    }
+    store_tile();
+    zero_acc();
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
-        acc[i][j] = mma(af[pl][i], bfr[pl][j], acc[i][j]);
-#pragma unroll
-        for (int q = i * T::FN + j; q < PER; q += NMF) load_one(q, kt % STAGES, koff);
-      }
-    __builtin_amdgcn_sched_barrier(0);
+    // First fragments of the next tile (after the last tile: unused).
+    read_frags(slot * STAGE, 0, pl ^ 1);
   }
-  // Last slice.
-  inner_steps(((KT - 1) % STAGES) * STAGE);
-  mfma_step(pl);
   // No load may still be writing LDS when the workgroup ends.
   wait_vmcnt<0>();
-
-  epilogue<T>(g, acc, m0 + wm * T::WTM, n0 + wn * T::WTN, lane);
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
 }
 
 }  // namespace gemm

@@ -59,6 +59,25 @@ def test_linear(L, m, n, k):
     np.testing.assert_allclose(f64(yf), ref, rtol=1e-4, atol=1e-4 * np.abs(ref).max())
 
 
+@pytest.mark.parametrize("m,n,k", [(520, 22528, 8192)])
+def test_linear_long_k_sampled_columns(L, m, n, k):
+    # The persistent ring kernel with the deep (5-slice) ring used for long
+    # products: 264 tiles (more than one per CU), a ragged last tile row.
+    # Reference on 192 sampled output columns.
+    x = syn.normal_bf16((m, k), 1.0, 13, f"lin.x.{m}.{k}")
+    w = syn.normal_bf16((n, k), 0.02, 14, f"lin.w.{n}.{k}")
+    say(f"linear long-k m={m} n={n} k={k}")
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    L.flux3_linear(dev(x), dev(w), y=y)
+    yf = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    L.flux3_linear(dev(x), dev(w), y_f32=yf)
+    torch.cuda.synchronize()
+    cols = np.sort(np.random.default_rng(5).choice(n, 192, replace=False))
+    ref = f64(x) @ f64(w[cols]).T
+    assert_agree(f64(y)[:, cols], ref, "linear long-k bf16")
+    np.testing.assert_allclose(f64(yf)[:, cols], ref, rtol=1e-4, atol=1e-4 * np.abs(ref).max())
+
+
 # ---- a2: modulation ----------------------------------------------------------------
 
 def test_modulate(L):
