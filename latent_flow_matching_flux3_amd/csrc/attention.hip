@@ -34,9 +34,10 @@ namespace flux3 {
 
 namespace {
 
-constexpr int kBQ = 128;   // query rows per workgroup
+constexpr int kBQ = 256;   // query rows per workgroup (8 waves x 32)
+constexpr int kWaves = kBQ / 32;
 constexpr int kBKV = 64;   // keys per tile
-constexpr int kNBuf = 4;   // LDS ring slots
+constexpr int kNBuf = 3;   // LDS ring slots
 constexpr int kTileChunks = kBKV * 16;  // 16-byte chunks of a 64 x 128 bf16 tile (16 KiB)
 constexpr float kSlack = 8.0f;          // allowed lag of the softmax reference max (log2 units)
 
@@ -63,7 +64,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kBQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict__ k, int ldk,
                      const bf16* __restrict__ v, int ldv, bf16* __restrict__ o, int ldo, int n,
                      float scale_log2) {
@@ -100,25 +101,26 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
   }
   const bf16x8* qw = qs_lds + wave * 512;
 
-  // Tile loads: each wave fills 4 KiB of K and 4 KiB of V per tile, 1 KiB
+  // Tile loads: each wave fills 2 KiB of K and 2 KiB of V per tile, 1 KiB
   // (4 key rows) per global_load_lds; lane t lands at row t/16, physical chunk
   // t%16 and so fetches the logical chunk that maps there.
   const int sub_row = lane >> 4, pchunk = lane & 15;
+  constexpr int kBlk = kBKV / 4 / kWaves;  // KiB blocks of K (and of V) per wave per tile
   auto issue_tile = [&](int tile, int slot) {
     const int key0 = min(tile, (n - 1) / kBKV) * kBKV;  // a tile past the end reloads the last one
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int row = (wave * 4 + b) * 4 + sub_row;   // 0..63
+    for (int b = 0; b < kBlk; ++b) {
+      const int row = (wave * kBlk + b) * 4 + sub_row;   // 0..63
       const int grow = min(key0 + row, n - 1);
       const int kc = pchunk ^ (row & 15);
       const int vc = pchunk ^ (4 * (row & 3));
       __builtin_amdgcn_global_load_lds((const gmem_void_t*)(k + (size_t)grow * ldk + hoff + kc * 8),
-                                       (lds_void_t*)(&ks_lds[slot][(wave * 4 + b) * 64]), 16, 0, 0);
+                                       (lds_void_t*)(&ks_lds[slot][(wave * kBlk + b) * 64]), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const gmem_void_t*)(v + (size_t)grow * ldv + hoff + vc * 8),
-                                       (lds_void_t*)(&vs_lds[slot][(wave * 4 + b) * 64]), 16, 0, 0);
+                                       (lds_void_t*)(&vs_lds[slot][(wave * kBlk + b) * 64]), 16, 0, 0);
     }
   };
-  constexpr int kLoadsPerTile = 8;  // per wave
+  constexpr int kLoadsPerTile = 2 * kBlk;  // per wave
 
   // S^T = K Q^T for one tile (two 32-key fragments, interleaved chains).
   auto scores = [&](int slot, floatx16 (&s)[2]) {
@@ -220,10 +222,10 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
   };
 
   const int ntiles = (n + kBKV - 1) / kBKV;
-  // Prologue: tiles 0..3 in flight, wait for 0 and 1, scores of tile 0.
+  // Prologue: tiles 0..2 in flight, wait for 0 and 1, scores of tile 0.
 #pragma unroll
   for (int t = 0; t < kNBuf; ++t) issue_tile(t, t);
-  wait_vmcnt<2 * kLoadsPerTile>();
+  wait_vmcnt<kLoadsPerTile>();
   __syncthreads();
   floatx16 sa[2], sb[2];
   bf16x8 pf[4];
@@ -239,9 +241,9 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
     scores((t + 1) % kNBuf, nxt);
     softmax(cur, t * kBKV, pf);
     pv(t % kNBuf, pf);
-    // Tile t+2 landed (only tile t+3 may still be in flight); after the
-    // barrier every wave is done with slot t % 4, which takes tile t+4.
-    wait_vmcnt<kLoadsPerTile>();
+    // Tile t+2 (the last one issued) landed; after the barrier every wave is
+    // done with slot t % 3, which takes tile t+3.
+    wait_vmcnt<0>();
     __syncthreads();
     issue_tile(t + kNBuf, t % kNBuf);
   };
@@ -275,7 +277,7 @@ void launch_attention(const bf16* q, int ldq, const bf16* k, int ldk, const bf16
   if (n <= 0) return;
   const int nqb = (n + kBQ - 1) / kBQ;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHeadDim);
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(nqb * kHeads), dim3(256), 0, st, q, ldq, k, ldk, v, ldv,
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(nqb * kHeads), dim3(kBQ * 2), 0, st, q, ldq, k, ldk, v, ldv,
                      o, ldo, n, scale_log2);
 }
 
