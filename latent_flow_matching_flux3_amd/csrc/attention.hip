@@ -5,13 +5,17 @@
 //
 // Design (gfx950, head_dim 128):
 //   - One workgroup = 4 waves = 128 query rows of one head; each wave owns 32
-//     query rows.  K and V are walked in 64-key tiles through a 4-slot LDS
-//     ring, filled straight from global memory (global_load_lds_dwordx4),
-//     three tiles ahead.
+//     query rows.  Two workgroups share a CU (80 KiB of LDS and at most 256
+//     registers per lane each), so each SIMD runs two waves of different
+//     workgroups: their per-tile barriers are independent, and one wave's
+//     softmax (VALU) overlaps the other's MFMAs.
+//   - K and V are walked in 32-key tiles through a 5-slot LDS ring, filled
+//     straight from global memory (global_load_lds_dwordx4), three to four
+//     tiles ahead.
 //   - Scores are formed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: A = K from LDS, B = Q^T held in registers for
-//     the whole kernel.  A lane then holds one query row (lane % 32) and 32 of
-//     the tile's 64 keys, so the row max and row sum are per-lane register
+//     the whole kernel.  A lane then holds one query row (lane % 32) and 16 of
+//     the tile's 32 keys, so the row max and row sum are per-lane register
 //     reductions plus one exchange between the wave halves.
 //   - The probabilities stay in registers and feed O^T = V^T P^T directly as
 //     the B operand (their register layout is already the B layout, with the
@@ -34,11 +38,11 @@ namespace flux3 {
 
 namespace {
 
-constexpr int kBQ = 256;   // query rows per workgroup (8 waves x 32)
+constexpr int kBQ = 128;   // query rows per workgroup (4 waves x 32)
 constexpr int kWaves = kBQ / 32;
-constexpr int kBKV = 64;   // keys per tile
-constexpr int kNBuf = 3;   // LDS ring slots
-constexpr int kTileChunks = kBKV * 16;  // 16-byte chunks of a 64 x 128 bf16 tile (16 KiB)
+constexpr int kBKV = 32;   // keys per tile
+constexpr int kNBuf = 5;   // LDS ring slots
+constexpr int kTileChunks = kBKV * 16;  // 16-byte chunks of a 32 x 128 bf16 tile (8 KiB)
 constexpr float kSlack = 8.0f;          // allowed lag of the softmax reference max (log2 units)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -68,9 +72,12 @@ __global__ __launch_bounds__(kBQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict__ k, int ldk,
                      const bf16* __restrict__ v, int ldv, bf16* __restrict__ o, int ldo, int n,
                      float scale_log2) {
-  __shared__ bf16x8 ks_lds[kNBuf][kTileChunks];
-  __shared__ bf16x8 vs_lds[kNBuf][kTileChunks];
-  __shared__ bf16x8 qs_lds[kBQ * 16];  // this workgroup's queries, 32 KiB
+  // One LDS object for both rings: with several, the compiler gives each its
+  // own alias scope and then waits for every tile load in flight before any
+  // LDS read that may alias one (the explicit waits below are exact).
+  __shared__ bf16x8 ring_lds[2 * kNBuf * kTileChunks];
+  bf16x8 (*ks_lds)[kTileChunks] = (bf16x8 (*)[kTileChunks])ring_lds;
+  bf16x8 (*vs_lds)[kTileChunks] = (bf16x8 (*)[kTileChunks])(ring_lds + kNBuf * kTileChunks);
 
   const int nqb = (n + kBQ - 1) / kBQ;
   const int total = nqb * kHeads;  // multiple of 8
@@ -84,22 +91,15 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
   const int lr = lane & 31, lh = lane >> 5;
   const int hoff = head * kHeadDim;
 
-  // Q of this wave's 32 rows goes to LDS once (same layout as a K tile, 16
-  // rows per 4 KiB... 32 rows = 8 KiB per wave); the Q^T fragments (B
-  // operand: query row lr, dims 16 s + 8 lh .. +8) are re-read per tile,
-  // which keeps them out of the register file.
+  // Q^T fragments of this wave's 32 rows, in registers for the whole kernel:
+  // the B operand of k-step st is query row lr, dims 16 st + 8 lh .. +8.
+  bf16x8 qf[8];
   {
-    const int sub = lane >> 4, pc = lane & 15;
+    const int grow = min(qb * kBQ + wave * 32 + lr, n - 1);
+    const bf16x8* qp = (const bf16x8*)(q + (size_t)grow * ldq + hoff);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int row = 4 * b + sub;  // 0..31 within the wave
-      const int grow = min(qb * kBQ + wave * 32 + row, n - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const gmem_void_t*)(q + (size_t)grow * ldq + hoff + (pc ^ (row & 15)) * 8),
-          (lds_void_t*)(&qs_lds[wave * 512 + b * 64]), 16, 0, 0);
-    }
+    for (int st = 0; st < 8; ++st) qf[st] = qp[2 * st + lh];
   }
-  const bf16x8* qw = qs_lds + wave * 512;
 
   // Tile loads: each wave fills 2 KiB of K and 2 KiB of V per tile, 1 KiB
   // (4 key rows) per global_load_lds; lane t lands at row t/16, physical chunk
@@ -110,7 +110,7 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
     const int key0 = min(tile, (n - 1) / kBKV) * kBKV;  // a tile past the end reloads the last one
 #pragma unroll
     for (int b = 0; b < kBlk; ++b) {
-      const int row = (wave * kBlk + b) * 4 + sub_row;   // 0..63
+      const int row = (wave * kBlk + b) * 4 + sub_row;   // 0..31
       const int grow = min(key0 + row, n - 1);
       const int kc = pchunk ^ (row & 15);
       const int vc = pchunk ^ (4 * (row & 3));
@@ -122,17 +122,13 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
   };
   constexpr int kLoadsPerTile = 2 * kBlk;  // per wave
 
-  // S^T = K Q^T for one tile (two 32-key fragments, interleaved chains).
-  auto scores = [&](int slot, floatx16 (&s)[2]) {
+  // S^T = K Q^T for one tile (one 32-key fragment).
+  auto scores = [&](int slot, floatx16& s) {
     const floatx16 zero = {};
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      const bf16x8 qf = qw[k_phys(lr, 2 * st + lh)];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = ks_lds[slot][k_phys(kb * 32 + lr, 2 * st + lh)];
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf, st == 0 ? zero : s[kb], 0, 0, 0);
-      }
+      const bf16x8 a = ks_lds[slot][k_phys(lr, 2 * st + lh)];
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], st == 0 ? zero : s, 0, 0, 0);
     }
   };
 
@@ -161,39 +157,64 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
     const int dim = 32 * db + tr_dim;
     tr_off[db] = v_phys(tr_key, dim >> 3) * 8 + (dim & 7);
   }
-  auto pv = [&](int slot, const bf16x8 (&pf)[4]) {
-    const bf16* base = (const bf16*)vs_lds[slot];
+  // The 16 transpose reads of a tile (4 head-dim blocks x 2 key groups x two
+  // 8-key halves) are issued as one batch and waited for inside the same asm
+  // block.  Through the builtin, the compiler would wait for every tile load
+  // in flight before the first of them; the explicit waits and barriers below
+  // already order them after the tile's data landed.
+  auto pv = [&](int slot, const bf16x8 (&pf)[2]) {
+    const unsigned base = (unsigned)(size_t)(lds_void_t*)vs_lds[slot];  // LDS byte address
+    unsigned addr[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int db = 0; db < 4; ++db) addr[db] = base + 2u * (unsigned)tr_off[db];
+    short4_t r[4][4];  // [db][j * 2 + half]
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %2, %16 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %3, %16 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %4, %17\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %6, %17 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %7, %17 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %8, %18\n\t"
+        "ds_read_b64_tr_b16 %9, %18 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %11, %18 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %12, %19\n\t"
+        "ds_read_b64_tr_b16 %13, %19 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %14, %19 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %15, %19 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]),
+          "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(r[1][2]), "=&v"(r[1][3]),
+          "=&v"(r[2][0]), "=&v"(r[2][1]), "=&v"(r[2][2]), "=&v"(r[2][3]),
+          "=&v"(r[3][0]), "=&v"(r[3][1]), "=&v"(r[3][2]), "=&v"(r[3][3])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3])
+        : "memory");
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16* p = base + tr_off[db] + 16 * j * kHeadDim;
-        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4_t*)(p));
-        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4_t*)(p + 8 * kHeadDim));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(r[db][2 * j], r[db][2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[j], oacc[db], 0, 0, 0);
       }
   };
 
   // Softmax of one tile: returns the probabilities as bf16 B operands and
   // updates m_run / l_run / oacc.
-  auto softmax = [&](floatx16 (&s)[2], int key0, bf16x8 (&pf)[4]) {
+  auto softmax = [&](floatx16& s, int key0, bf16x8 (&pf)[2]) {
     if (key0 + kBKV > n) {  // keys past the end get probability 0
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          if (key >= n) s[kb][r] = -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (key >= n) s[r] = -INFINITY;
+      }
     }
-    float mx = s[0][0];
+    float mx = s[0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = half_max(mx) * scale_log2;
     // The reference max may lag the true running max by up to kSlack (base 2),
     // so probabilities stay <= 2^kSlack; O and l share the reference, so the
@@ -211,45 +232,51 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
     }
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -m_run));
-        psum += p;
-        pf[kb * 2 + (r >> 3)][r & 7] = to_bf16(p);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m_run));
+      psum += p;
+      pf[r >> 3][r & 7] = to_bf16(p);
+    }
     l_run += psum;
   };
 
   const int ntiles = (n + kBKV - 1) / kBKV;
-  // Prologue: tiles 0..2 in flight, wait for 0 and 1, scores of tile 0.
+  // Prologue: tiles 0..4 in flight, wait for 0 and 1, scores of tile 0.
 #pragma unroll
   for (int t = 0; t < kNBuf; ++t) issue_tile(t, t);
-  wait_vmcnt<kLoadsPerTile>();
+  wait_vmcnt<(kNBuf - 2) * kLoadsPerTile>();
   __syncthreads();
-  floatx16 sa[2], sb[2];
-  bf16x8 pf[4];
+  floatx16 sa, sb;
+  bf16x8 pf[2];
   scores(0, sa);
 
-  // One iteration: scores of tile t+1 into `nxt` while the softmax of tile t
-  // (in `cur`) runs, then P V of tile t, then the ring advances.
-  // Every step is unconditional (straight-line loop body): a tile index past
-  // the end reloads the last tile, and a step on such a tile masks all of its
-  // keys, so it adds nothing.  Steps come in pairs (the score buffers swap
-  // roles), so an odd tile count runs one fully masked step.
-  auto step = [&](int t, floatx16 (&cur)[2], floatx16 (&nxt)[2]) {
+  // One step: scores of tile t+1 into `nxt` while the softmax of tile t (in
+  // `cur`) runs, then P V of tile t; then wait until tile t+2 has landed for
+  // every wave.  Steps come in pairs (the score buffers swap roles) and the
+  // ring is refilled once per pair, at its end, with the two tiles whose
+  // slots the pair freed: a tile load is then never followed by an LDS read
+  // in the same loop iteration (the compiler would otherwise wait for every
+  // load in flight before that read).  Every step is unconditional: a tile
+  // index past the end reloads the last tile, and a step on such a tile masks
+  // all of its keys, so it adds nothing; an odd tile count runs one fully
+  // masked step.
+  auto step = [&](int t, floatx16& cur, floatx16& nxt) {
     scores((t + 1) % kNBuf, nxt);
     softmax(cur, t * kBKV, pf);
     pv(t % kNBuf, pf);
-    // Tile t+2 (the last one issued) landed; after the barrier every wave is
-    // done with slot t % 3, which takes tile t+3.
-    wait_vmcnt<0>();
-    __syncthreads();
-    issue_tile(t + kNBuf, t % kNBuf);
   };
   for (int t = 0; t < ntiles; t += 2) {
     step(t, sa, sb);
+    // Tile t+2 landed (tiles t+3 and t+4 may still be in flight).
+    wait_vmcnt<2 * kLoadsPerTile>();
+    __syncthreads();
     step(t + 1, sb, sa);
+    // Tile t+3 landed (tile t+4 may still be in flight); every wave is done
+    // with the slots of tiles t and t+1, which take tiles t+5 and t+6.
+    wait_vmcnt<kLoadsPerTile>();
+    __syncthreads();
+    issue_tile(t + kNBuf, t % kNBuf);
+    issue_tile(t + 1 + kNBuf, (t + 1) % kNBuf);
   }
   wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
 
