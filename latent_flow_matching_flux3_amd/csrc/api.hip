@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/flux3_dit.h"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -58,15 +60,21 @@ bf16* B(uint16_t* p) { return reinterpret_cast<bf16*>(p); }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Block workspace: xm [n][3072] | qkv [n][9216] | cat [n][12288], bf16.
+// The q|k|v region is dead once attention has run, so the output projection
+// borrows it as scratch for a K-split product (sized for that too).
 struct BlockWs {
   bf16* xm;
   bf16* qkv;
+  size_t qkv_bytes;
   bf16* cat;
 };
 
+size_t qkv_region_bytes(int n) {
+  return align256(std::max((size_t)n * 3 * kHidden * 2, gemm_split_ws_bytes(n, kHidden, kWOutCols)));
+}
+
 size_t block_ws_bytes(int n) {
-  return align256((size_t)n * kHidden * 2) + align256((size_t)n * 3 * kHidden * 2) +
-         align256((size_t)n * kWOutCols * 2);
+  return align256((size_t)n * kHidden * 2) + qkv_region_bytes(n) + align256((size_t)n * kWOutCols * 2);
 }
 
 BlockWs carve_block_ws(void* ws, int n) {
@@ -75,7 +83,8 @@ BlockWs carve_block_ws(void* ws, int n) {
   w.xm = (bf16*)p;
   p += align256((size_t)n * kHidden * 2);
   w.qkv = (bf16*)p;
-  p += align256((size_t)n * 3 * kHidden * 2);
+  w.qkv_bytes = qkv_region_bytes(n);
+  p += w.qkv_bytes;
   w.cat = (bf16*)p;
   return w;
 }
@@ -109,7 +118,7 @@ void in_proj(const bf16* xm, int n, const bf16* w_in, bf16* qkv, bf16* h, int ld
 
 // a8: x += gate * ([o | h] [W_o | W_out]^T).
 void out_proj(const bf16* cat, int n, const bf16* w_out, float* x, const SegTable& seg,
-              const float* mod, hipStream_t st) {
+              const float* mod, hipStream_t st, void* scratch = nullptr, size_t scratch_bytes = 0) {
   GemmArgs o{};
   o.A = cat;
   o.lda = kWOutCols;
@@ -125,6 +134,8 @@ void out_proj(const bf16* cat, int n, const bf16* w_out, float* x, const SegTabl
   o.mod_stride = 3 * kHidden;
   o.gate_offset = 2 * kHidden;
   o.seg = seg;
+  o.split_ws = scratch;
+  o.split_ws_bytes = scratch_bytes;
   launch_gemm(o, st);
 }
 
@@ -143,7 +154,7 @@ void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
   launch_attention(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, ws.qkv + 2 * kHidden,
                    3 * kHidden, ws.cat, kWOutCols, n, st);
   // a8: gated residual
-  out_proj(ws.cat, n, B(w->w_out), x, seg, mod, st);
+  out_proj(ws.cat, n, B(w->w_out), x, seg, mod, st, ws.qkv, ws.qkv_bytes);
 }
 
 }  // namespace
@@ -579,6 +590,8 @@ int flux3_stack_forward(const flux3_model_weights* w, const uint16_t* img, int n
     g.epi = GemmEpi::kStoreF32;
     g.C = s.x + (size_t)row0[i] * kHidden;
     g.ldc = kHidden;
+    g.split_ws = bws.qkv;  // free until the first block
+    g.split_ws_bytes = bws.qkv_bytes;
     launch_gemm(g, stream);
   }
 

@@ -45,7 +45,8 @@ void launch_ring(const GemmArgs& g, hipStream_t st) {
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = g.N / BN;
   const int total = tiles_m * tiles_n;
-  const int grid = std::min(total, cu_count() * WPE);
+  const int items = total * (EPI == GemmEpi::kSplitPartial ? g.ksplit : 1);
+  const int grid = std::min(items, cu_count() * WPE);
   hipLaunchKernelGGL((gemm::gemm_ring_kernel<BM, BN, WM, WN, BK, ST, WPE, EPI>), dim3(grid),
                      dim3(WM * WN * 64), 0, st, g, tiles_m, tiles_n);
 }
@@ -57,10 +58,67 @@ void run_ring(const GemmArgs& g, hipStream_t st) {
     case GemmEpi::kStoreF32: launch_ring<BM, BN, WM, WN, BK, ST, WPE, GemmEpi::kStoreF32>(g, st); break;
     case GemmEpi::kInProj: launch_ring<BM, BN, WM, WN, BK, ST, WPE, GemmEpi::kInProj>(g, st); break;
     case GemmEpi::kGatedResidual: launch_ring<BM, BN, WM, WN, BK, ST, WPE, GemmEpi::kGatedResidual>(g, st); break;
+    case GemmEpi::kSplitPartial:
+      launch_ring<BM, BN, WM, WN, BK, ST, WPE, GemmEpi::kSplitPartial>(g, st);
+      break;
   }
 }
 
+// K ranges for a split product on 256x256 tiles: the largest
+// divisor s of K/32 with s * tiles <= CUs and ranges of at least 16 slices of
+// 32; 1 when the product already has 128 tiles or more.
+int split_count(int m, int n, int k) {
+  if (n % 256 != 0 || k % 32 != 0) return 1;
+  const long tiles = (long)((m + 255) / 256) * (n / 256);
+  if (tiles >= 128) return 1;
+  const int kt = k / 32;
+  int best = 1;
+  for (int s = 2; s <= kt / 16; ++s)
+    if (kt % s == 0 && tiles * s <= cu_count()) best = s;
+  return best;
+}
+
+size_t split_bytes(int m, int n, int s) { return (size_t)s * ((m + 255) / 256) * 256 * n * 4; }
+
+// Sum of the K-range partials, four columns per thread: gated (mod != null)
+// x[r][c] += gate[seg(r)][c] * sum_s part[s][r][c], else x[r][c] = sum.
+__global__ __launch_bounds__(256) void split_reduce_kernel(float* x, int ldx, const float* part,
+                                                           size_t stride, int splits, int m, int n,
+                                                           const float* mod, int mod_stride,
+                                                           int gate_offset, SegTable seg) {
+  const int quads = n / 4;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)m * quads) return;
+  const int r = (int)(idx / quads), c = (int)(idx % quads) * 4;
+  const float* p = part + (size_t)r * n + c;
+  float4 acc = *(const float4*)p;
+  for (int sp = 1; sp < splits; ++sp) {
+    const float4 t = *(const float4*)(p + sp * stride);
+    acc.x += t.x;
+    acc.y += t.y;
+    acc.z += t.z;
+    acc.w += t.w;
+  }
+  float4* xp = (float4*)(x + (size_t)r * ldx + c);
+  if (mod == nullptr) {
+    *xp = acc;
+    return;
+  }
+  const float4 gt = *(const float4*)(mod + (size_t)seg_of_row(seg, r) * mod_stride + gate_offset + c);
+  float4 xv = *xp;
+  xv.x += gt.x * acc.x;
+  xv.y += gt.y * acc.y;
+  xv.z += gt.z * acc.z;
+  xv.w += gt.w * acc.w;
+  *xp = xv;
+}
+
 }  // namespace
+
+size_t gemm_split_ws_bytes(int m, int n, int k) {
+  const int s = split_count(m, n, k);
+  return s > 1 ? split_bytes(m, n, s) : 0;
+}
 
 // Tile choice: 256x256 tiles on the persistent ring kernel (4 waves, 128x128
 // per wave) when there are at least 192 of them; otherwise the register-staged
@@ -70,6 +128,28 @@ void run_ring(const GemmArgs& g, hipStream_t st) {
 void launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 0) return;
   const long big_tiles = (long)((g.M + 255) / 256) * (g.N / 256);
+  // Gated residual and fp32 products with too few tiles to fill the chip and
+  // a long K (the text stream's and small batches' output projection, the text
+  // embedding): split K over the idle CUs when the caller lent scratch for the
+  // partial products.
+  const bool gated = g.epi == GemmEpi::kGatedResidual;
+  if ((gated || g.epi == GemmEpi::kStoreF32) && g.split_ws != nullptr) {
+    const int s = split_count(g.M, g.N, g.K);
+    if (s > 1 && split_bytes(g.M, g.N, s) <= g.split_ws_bytes) {
+      GemmArgs h = g;
+      h.epi = GemmEpi::kSplitPartial;
+      h.ksplit = s;
+      h.C = g.split_ws;
+      h.ldc = g.N;
+      run_ring<256, 256, 2, 2, 32, 5, 1>(h, st);
+      const size_t stride = (size_t)((g.M + 255) / 256) * 256 * g.N;
+      const size_t quads = (size_t)g.M * (g.N / 4);
+      hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st,
+                         (float*)g.C, g.ldc, (const float*)g.split_ws, stride, s, g.M, g.N,
+                         gated ? g.mod : nullptr, g.mod_stride, g.gate_offset, g.seg);
+      return;
+    }
+  }
   if (g.N % 256 == 0 && big_tiles >= 192) {
     // Long products (the block's output projection, K = 12288) keep more
     // slices in flight: five 32-wide slices instead of two 64-wide ones.

@@ -110,6 +110,14 @@ struct TileWalk {
   __device__ __forceinline__ void coords(int i, int tiles_m, int tiles_n, int& tm, int& tn) const {
     grouped_coords(lo + first + i * step, tiles_m, tiles_n, tm, tn);
   }
+  // Work item i when each tile is split into `splits` K ranges (consecutive
+  // items are the ranges of one tile).
+  __device__ __forceinline__ void coords(int i, int tiles_m, int tiles_n, int splits, int& tm, int& tn,
+                                         int& split) const {
+    const int lin = lo + first + i * step;
+    split = lin % splits;
+    grouped_coords(lin / splits, tiles_m, tiles_n, tm, tn);
+  }
 };
 
 // Epilogue of one wave's WTM x WTN accumulator tile (rows wrow0.., columns
@@ -190,6 +198,21 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::F
                 make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
                             acc[i][j][4 * g4 + 3]);
       }
+    }
+  } else if constexpr (EPI == GemmEpi::kSplitPartial) {
+    // fp32 partial product of one K range into the split scratch (rows of a
+    // ragged last tile land in padding that is never read).
+    float* C = (float*)g.C;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      float* crow = C + (size_t)(wrow0 + 32 * i + lr) * g.ldc + wcol0;
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *(float4*)(crow + 32 * j + frag_col(g4, lane)) =
+              make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                          acc[i][j][4 * g4 + 3]);
     }
   } else {
     static_assert(EPI == GemmEpi::kGatedResidual, "epilogue kind");
@@ -397,7 +420,8 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   static_assert(KSTEPS >= 2, "BK >= 32");
   __shared__ bf16x8 lds[STAGES * STAGE];
 
-  const TileWalk walk(tiles_m * tiles_n);
+  const int splits = EPI == GemmEpi::kSplitPartial ? g.ksplit : 1;
+  const TileWalk walk(tiles_m * tiles_n * splits);
   if (walk.count == 0) return;
 
   const int tid = threadIdx.x;
@@ -420,12 +444,14 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   }
   const char* a_tile;
   const char* b_tile;
+  const int KT = g.K / BK / splits;  // K slices per work item, >= 1
   auto set_src = [&](int i) {
-    int tm, tn;
-    walk.coords(i, tiles_m, tiles_n, tm, tn);
+    int tm, tn, split;
+    walk.coords(i, tiles_m, tiles_n, splits, tm, tn, split);
     const int m0 = tm * BM;
-    a_tile = (const char*)(g.A + (size_t)m0 * g.lda);
-    b_tile = (const char*)(g.B + (size_t)tn * BN * g.ldb);
+    const size_t k0 = (size_t)split * KT * BK;
+    a_tile = (const char*)(g.A + (size_t)m0 * g.lda + k0);
+    b_tile = (const char*)(g.B + (size_t)tn * BN * g.ldb + k0);
 #pragma unroll
     for (int q = 0; q < A_BLK; ++q) {
       const int row = (wave * A_BLK + q) * Lay::RPB + sub_row;
@@ -449,7 +475,6 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   // every refill still issues PER loads (the final slice again, into buffers
   // that are no longer read), so the count of loads in flight behind a given
   // slice is constant.
-  const int KT = g.K / BK;  // >= 1
   int ld_i = 0, ld_kt = 0;
   auto advance_load = [&]() {
     if (++ld_kt == KT) {
@@ -514,9 +539,9 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   // runs between the last MFMA and the stores.
   int out_row = 0, out_col = 0;
   auto set_out = [&](int i) {
-    int tm, tn;
-    walk.coords(i, tiles_m, tiles_n, tm, tn);
-    out_row = __builtin_amdgcn_readfirstlane(tm * BM + wm * T::WTM);
+    int tm, tn, split;
+    walk.coords(i, tiles_m, tiles_n, splits, tm, tn, split);
+    out_row = __builtin_amdgcn_readfirstlane(split * tiles_m * BM + tm * BM + wm * T::WTM);
     out_col = __builtin_amdgcn_readfirstlane(tn * BN + wn * T::WTN);
   };
   auto store_tile = [&]() { epilogue<T, EPI>(g, acc, out_row, out_col); };

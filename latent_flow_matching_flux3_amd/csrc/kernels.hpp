@@ -16,7 +16,12 @@ enum class GemmEpi {
   kStoreBf16,     // C bf16 [M][N], stride ldc
   kStoreF32,      // C fp32 [M][N], stride ldc
   kInProj,        // cols < 9216: q|k|v store; cols >= 9216: SwiGLU of interleaved a/b -> h
-  kGatedResidual  // x[row][col] += gate[seg(row)][col] * acc, x fp32
+  kGatedResidual,  // x[row][col] += gate[seg(row)][col] * acc, x fp32
+  // One of ksplit K ranges of a kGatedResidual or kStoreF32 product: the
+  // fp32 partial product goes to rows split * Mpad + row of C (Mpad = M
+  // rounded up to the tile height); a reduction kernel then adds
+  // gate * (sum of the partials) to x, or stores the sum.
+  kSplitPartial
 };
 
 struct GemmArgs {
@@ -37,7 +42,17 @@ struct GemmArgs {
   int mod_stride;
   int gate_offset;
   SegTable seg;
+  // kGatedResidual / kStoreF32: optional scratch that lets a product with too
+  // few tiles to fill the chip be split over K (null: no split).
+  void* split_ws;
+  size_t split_ws_bytes;
+  // kSplitPartial: number of K ranges (divides K / 32)
+  int ksplit;
 };
+
+// Scratch bytes a kGatedResidual or kStoreF32 product of this shape uses when
+// split over K (0: it is not split).
+size_t gemm_split_ws_bytes(int m, int n, int k);
 
 void launch_ln_modulate(const float* x, int ldx, bf16* out, int ldo, int n, const SegTable& seg,
                         const float* mod, int mod_stride, hipStream_t st);
