@@ -241,19 +241,19 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
   };
 
   const int ntiles = (n + kBKV - 1) / kBKV;
-  // Prologue: tiles 0..4 in flight, wait for 0 and 1, scores of tile 0.
+  // Prologue: tiles 0..4 in flight, wait for 0, 1 and 2, scores of tile 0.
 #pragma unroll
   for (int t = 0; t < kNBuf; ++t) issue_tile(t, t);
-  wait_vmcnt<(kNBuf - 2) * kLoadsPerTile>();
+  wait_vmcnt<(kNBuf - 3) * kLoadsPerTile>();
   __syncthreads();
   floatx16 sa, sb;
   bf16x8 pf[2];
   scores(0, sa);
 
   // One step: scores of tile t+1 into `nxt` while the softmax of tile t (in
-  // `cur`) runs, then P V of tile t; then wait until tile t+2 has landed for
-  // every wave.  Steps come in pairs (the score buffers swap roles) and the
-  // ring is refilled once per pair, at its end, with the two tiles whose
+  // `cur`) runs, then P V of tile t.  Steps come in pairs (the score buffers
+  // swap roles); a pair starts with tiles t .. t+2 landed for every wave, and
+  // the ring is refilled once per pair, at its end, with the two tiles whose
   // slots the pair freed: a tile load is then never followed by an LDS read
   // in the same loop iteration (the compiler would otherwise wait for every
   // load in flight before that read).  Every step is unconditional: a tile
@@ -267,13 +267,10 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
   };
   for (int t = 0; t < ntiles; t += 2) {
     step(t, sa, sb);
-    // Tile t+2 landed (tiles t+3 and t+4 may still be in flight).
-    wait_vmcnt<2 * kLoadsPerTile>();
-    __syncthreads();
     step(t + 1, sb, sa);
-    // Tile t+3 landed (tile t+4 may still be in flight); every wave is done
-    // with the slots of tiles t and t+1, which take tiles t+5 and t+6.
-    wait_vmcnt<kLoadsPerTile>();
+    // Tiles t+3 and t+4 landed; every wave is done with the slots of tiles t
+    // and t+1, which take tiles t+5 and t+6.
+    wait_vmcnt<0>();
     __syncthreads();
     issue_tile(t + kNBuf, t % kNBuf);
     issue_tile(t + 1 + kNBuf, (t + 1) % kNBuf);
