@@ -524,13 +524,20 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   // current step were read a whole step earlier; waiting for them before
   // issuing the next reads keeps at most FM + FN reads outstanding (lgkmcnt
   // only counts to 15) and costs nothing.
+  static_assert(NMF % (T::FM + T::FN) == 0, "MFMAs per fragment read");
   auto inner_steps = [&](int cur) {
 #pragma unroll
     for (int ks = 0; ks + 1 < KSTEPS; ++ks) {
       __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
       read_frags(cur, ks + 1, (ks & 1) ^ 1);
-      __builtin_amdgcn_sched_barrier(0);
       mfma_step(ks & 1);
+      // One fragment read, then its share of the MFMAs, so the read burst
+      // never leaves the MFMA pipe without work.
+#pragma unroll
+      for (int q = 0; q < T::FM + T::FN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF / (T::FM + T::FN), 0);  // MFMA
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
