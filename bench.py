@@ -155,6 +155,39 @@ def event_time_ms(torch, fn, reps: int) -> float:
     return a.elapsed_time(b) / reps
 
 
+def sampler_loop(L, torch, model, img, txt, table, n_img: int, n_txt: int, steps: int):
+    """The whole sampling loop (steps flow-map steps) as one flux3_sample call,
+    timed eagerly and as one captured HIP graph (3 timed runs each)."""
+    ws = L.workspace(L.flux3_sample_workspace_size(n_img, 0, n_txt))
+    x0 = img.float().contiguous()
+    x = x0.clone()
+    sig = L.flux3_sigmas(steps)
+
+    def run():
+        L.flux3_sample(model, x, None, txt, table, sig, ws)
+
+    eager = event_time_ms(torch, run, 3)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    graph_ms = event_time_ms(torch, graph.replay, 3)
+    x.copy_(x0)
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.isfinite(x).all().item(), "non-finite sample"
+    del graph
+    n = n_img + n_txt
+    return {"tokens": n, "steps": steps, "eager_ms_per_image": round(eager, 3),
+            "graph_ms_per_image": round(graph_ms, 3), "graph_steps_per_s": round(steps * 1e3 / graph_ms, 2),
+            "graph_tflops": round(steps * stack_flops(n_img, 0, n_txt) / (graph_ms * 1e-3) / 1e12, 1)}
+
+
 def cpu_baseline(seed: int):
     """The CPU oracle (float64 NumPy), untuned, on a bounded sample: one joint
     block at 4608 tokens (image 64x64 + 512 text), two modulation segments."""
@@ -285,6 +318,15 @@ def main():
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
 
+    print("[bench] 16-step sampler loop: one flux3_sample call, eager and as a HIP graph",
+          file=sys.stderr, flush=True)
+    loops = {"4608tok": sampler_loop(L, torch, model, img, txt, table, n_img, n_txt, 16)}
+    small = syn.WORKLOADS["block_128px_96tok"]
+    s_img = syn.latents(args.seed + 3, small.n_img).to("cuda")
+    s_txt = syn.text_features(args.seed + 4, small.n_txt).to("cuda")
+    s_table = L.flux3_rope_table(L.flux3_build_ids(small.img_h, small.img_w, small.n_txt).to("cuda"))
+    loops["96tok"] = sampler_loop(L, torch, model, s_img, s_txt, s_table, small.n_img, small.n_txt, 16)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle, one block)", file=sys.stderr, flush=True)
@@ -312,6 +354,7 @@ def main():
                    "sampler": "flow map, 16-step shifted schedule (alpha 6.93)", "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "kernels": per_kernel,
+        "sampler_loop": loops,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -194,6 +194,18 @@ WORKLOADS = {
     "stack_4ref_1024_20992tok": Layout(64, 64, 512, [(64, 64)] * 4),
 }
 
+# The token counts of the blog's tokens-per-call chart (What it costs to run):
+# image tokens, references at their own size, and text padded to a multiple of
+# 80 (the text lengths are what the chart's totals leave; the features are
+# random stand-ins for a prompt of that padded length).  1360x768 px is an
+# 85-wide, 48-high token grid.
+PAGE_WORKLOADS = {
+    "block_t2i_1024_page_4256tok": Layout(64, 64, 160),
+    "block_i2i_1024_page_8272tok": Layout(64, 64, 80, [(64, 64)]),
+    "block_layout_t2i_1024_page_4336tok": Layout(64, 64, 240),
+    "block_layout_i2i_1360x768_page_8800tok": Layout(48, 85, 640, [(48, 85)]),
+}
+
 
 def block_activations(seed: int, n: int) -> torch.Tensor:
     """Residual-stream input of one block, N(0,1) bf16 [n, 3072]."""

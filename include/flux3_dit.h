@@ -285,6 +285,26 @@ int flux3_stack_forward(const flux3_model_weights* w, const uint16_t* img, int n
 int flux3_euler_step(float* x, uint16_t* x_bf16, const float* v, int n, float sigma,
                      float sigma_next, hipStream_t stream);
 
+/* flux3_sample: the whole flow-map sampling loop in one call ([issue]
+ * "Sampling"; [blog] "The denoising loop"): for k = 0..steps-1,
+ *   v = flux3_stack_forward(bf16(x), sigmas[k], sigmas[k+1]);
+ *   x <- x + (sigmas[k+1] - sigmas[k]) v.
+ * Everything is enqueued on `stream` with no host synchronisation and no
+ * allocation, so the call can be captured into one HIP graph by the caller
+ * (the sigmas are read on the host at call time and baked into the launches).
+ *   x      : device [n_img][128] fp32 latents, in/out (the final x on return)
+ *   cond, txt, table : as for flux3_stack_forward, constant over the loop
+ *   sigmas : host [steps+1] fp32 (e.g. from flux3_sigmas), all finite
+ *   steps  : >= 0 (0 leaves x untouched)
+ *   workspace : device, >= flux3_sample_workspace_size(n_img, n_cond, n_txt)
+ * The result equals steps calls of flux3_stack_forward + flux3_euler_step
+ * bit for bit. */
+size_t flux3_sample_workspace_size(int n_img, int n_cond, int n_txt);
+int flux3_sample(const flux3_model_weights* w, float* x, int n_img, const uint16_t* cond,
+                 int n_cond, const uint16_t* txt, int n_txt, const float* table,
+                 const float* sigmas, int steps, void* workspace, size_t ws_bytes,
+                 hipStream_t stream);
+
 /* flux3_sigmas: the shifted schedule, host only ([issue] "Sampling"):
  * t_k = 1 - k/steps, sigma_k = alpha t_k / (1 + (alpha - 1) t_k), k = 0..steps.
  *   out: host [steps+1] fp32 (computed in fp64). */

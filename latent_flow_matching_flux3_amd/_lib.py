@@ -73,6 +73,8 @@ _SIGS = {
     "flux3_time_vectors": (I, [P, P, P, P, F, F, P, I, P, P, S, P]),
     "flux3_stack_workspace_size": (S, [I, I, I]),
     "flux3_stack_forward": (I, [C.POINTER(ModelWeightsC), P, I, P, I, P, I, P, F, F, P, P, S, P]),
+    "flux3_sample_workspace_size": (S, [I, I, I]),
+    "flux3_sample": (I, [C.POINTER(ModelWeightsC), P, I, P, I, P, I, P, P, I, P, S, P]),
     "flux3_euler_step": (I, [P, P, P, I, F, F, P]),
     "flux3_sigmas": (I, [I, C.c_double, P]),
 }
@@ -306,6 +308,23 @@ def flux3_stack_forward(weights: ModelWeights, img, cond, txt, table, sigma, sig
                                      _ptr(v), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream)))
     return v
+
+
+def flux3_sample_workspace_size(n_img: int, n_cond: int, n_txt: int) -> int:
+    return lib().flux3_sample_workspace_size(n_img, n_cond, n_txt)
+
+
+def flux3_sample(weights: ModelWeights, x, cond, txt, table, sigmas, workspace, stream=None):
+    """x: device [n_img, 128] fp32, updated in place; sigmas: [steps + 1] host values."""
+    _require_dev(x, torch.float32, "x")
+    sig = torch.as_tensor(sigmas, dtype=torch.float32).cpu().contiguous()
+    n_cond = 0 if cond is None else cond.shape[0]
+    n_txt = 0 if txt is None else txt.shape[0]
+    _check(lib().flux3_sample(C.byref(weights.c), _ptr(x), x.shape[0], _ptr(cond), n_cond,
+                              _ptr(txt), n_txt, _ptr(table), sig.data_ptr(), sig.numel() - 1,
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream)))
+    return x
 
 
 def flux3_euler_step(x, x_bf16, v, sigma, sigma_next, stream=None):

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "../../include/flux3_dit.h"
 #include "common.hpp"
@@ -485,10 +486,14 @@ size_t flux3_stack_workspace_size(int n_img, int n_cond, int n_txt) {
   return stack_ws_bytes((int)n);
 }
 
-int flux3_stack_forward(const flux3_model_weights* w, const uint16_t* img, int n_img,
-                        const uint16_t* cond, int n_cond, const uint16_t* txt, int n_txt,
-                        const float* table, float sigma, float sigma_next, float* v,
-                        void* workspace, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// Argument checks shared by flux3_stack_forward and flux3_sample (everything
+// but the workspace size).
+int check_stack_args(const flux3_model_weights* w, const uint16_t* img, int n_img,
+                     const uint16_t* cond, int n_cond, const uint16_t* txt, int n_txt,
+                     const float* table, const float* v, const void* workspace) {
   REQUIRE(w != nullptr, FLUX3_EINVAL, "weights are null");
   REQUIRE(n_img > 0 && n_cond >= 0 && n_txt >= 0, FLUX3_EINVAL, "n_img=%d n_cond=%d n_txt=%d",
           n_img, n_cond, n_txt);
@@ -508,22 +513,10 @@ int flux3_stack_forward(const flux3_model_weights* w, const uint16_t* img, int n
           "ref_time_in weights: give both or neither");
   REQUIRE_PTR(w->final_ada);
   REQUIRE_PTR(w->final_linear);
-  const int n_total = n_img + n_cond + n_txt;
   REQUIRE(workspace != nullptr && aligned16(workspace), FLUX3_EWORKSPACE, "workspace missing");
-  REQUIRE(ws_bytes >= stack_ws_bytes(n_total), FLUX3_EWORKSPACE, "workspace %zu < %zu bytes",
-          ws_bytes, stack_ws_bytes(n_total));
-
-  // Streams present, in token order.
-  int modes[3], counts[3], n_modes = 0;
   const int all_counts[3] = {n_img, n_cond, n_txt};
-  for (int m = 0; m < 3; ++m)
-    if (all_counts[m] > 0) {
-      modes[n_modes] = m;
-      counts[n_modes] = all_counts[m];
-      ++n_modes;
-    }
-  for (int i = 0; i < n_modes; ++i) {
-    const int m = modes[i];
+  for (int m = 0; m < 3; ++m) {
+    if (all_counts[m] == 0) continue;
     REQUIRE(w->early_mod[m] && aligned16(w->early_mod[m]), FLUX3_EINVAL, "early_mod[%d] missing", m);
     REQUIRE(w->single_mod[m] && aligned16(w->single_mod[m]), FLUX3_EINVAL, "single_mod[%d] missing", m);
     REQUIRE(w->n_early == 0 || w->early[m] != nullptr, FLUX3_EINVAL, "early[%d] missing", m);
@@ -537,6 +530,24 @@ int flux3_stack_forward(const flux3_model_weights* w, const uint16_t* img, int n
     int rc = check_block_weights(&w->single[b]);
     if (rc) return rc;
   }
+  return FLUX3_OK;
+}
+
+// One pass of the transformer on checked arguments; workspace = StackWs.
+int stack_forward_unchecked(const flux3_model_weights* w, const uint16_t* img, int n_img,
+                            const uint16_t* cond, int n_cond, const uint16_t* txt, int n_txt,
+                            const float* table, float sigma, float sigma_next, float* v,
+                            void* workspace, hipStream_t stream) {
+  const int n_total = n_img + n_cond + n_txt;
+  // Streams present, in token order.
+  int modes[3], counts[3], n_modes = 0;
+  const int all_counts[3] = {n_img, n_cond, n_txt};
+  for (int m = 0; m < 3; ++m)
+    if (all_counts[m] > 0) {
+      modes[n_modes] = m;
+      counts[n_modes] = all_counts[m];
+      ++n_modes;
+    }
 
   StackWs s = carve_stack_ws(workspace, n_total);
   const BlockWs bws = carve_block_ws(s.block_ws, n_total);
@@ -634,6 +645,67 @@ int flux3_stack_forward(const flux3_model_weights* w, const uint16_t* img, int n
   f.ldc = 128;
   launch_gemm(f, stream);
   return check_launch("stack_forward");
+}
+
+// flux3_sample's workspace: the stack's, then v [n_img][128] fp32 and the
+// bf16 copy of x [n_img][128] the embedding reads.
+size_t sample_ws_bytes(int n_img, int n_total) {
+  return stack_ws_bytes(n_total) + align256((size_t)n_img * 128 * 4) +
+         align256((size_t)n_img * 128 * 2);
+}
+}  // namespace
+
+extern "C" {
+
+int flux3_stack_forward(const flux3_model_weights* w, const uint16_t* img, int n_img,
+                        const uint16_t* cond, int n_cond, const uint16_t* txt, int n_txt,
+                        const float* table, float sigma, float sigma_next, float* v,
+                        void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_stack_args(w, img, n_img, cond, n_cond, txt, n_txt, table, v, workspace);
+  if (rc) return rc;
+  const int n_total = n_img + n_cond + n_txt;
+  REQUIRE(ws_bytes >= stack_ws_bytes(n_total), FLUX3_EWORKSPACE, "workspace %zu < %zu bytes",
+          ws_bytes, stack_ws_bytes(n_total));
+  return stack_forward_unchecked(w, img, n_img, cond, n_cond, txt, n_txt, table, sigma,
+                                 sigma_next, v, workspace, stream);
+}
+
+size_t flux3_sample_workspace_size(int n_img, int n_cond, int n_txt) {
+  const long n = (long)n_img + n_cond + n_txt;
+  if (n_img <= 0 || n_cond < 0 || n_txt < 0 || n >= (1L << 30)) return 0;
+  return sample_ws_bytes(n_img, (int)n);
+}
+
+int flux3_sample(const flux3_model_weights* w, float* x, int n_img, const uint16_t* cond,
+                 int n_cond, const uint16_t* txt, int n_txt, const float* table,
+                 const float* sigmas, int steps, void* workspace, size_t ws_bytes,
+                 hipStream_t stream) {
+  REQUIRE(steps >= 0, FLUX3_EINVAL, "steps=%d", steps);
+  REQUIRE(steps == 0 || sigmas != nullptr, FLUX3_EINVAL, "sigmas is null");
+  for (int k = 0; k <= steps && steps > 0; ++k)
+    REQUIRE(std::isfinite(sigmas[k]), FLUX3_EINVAL, "sigmas[%d] is not finite", k);
+  REQUIRE_PTR(x);
+  // x doubles as the velocity pointer for the shared checks (only non-null
+  // and alignment are checked there).
+  int rc = check_stack_args(w, (const uint16_t*)x, n_img, cond, n_cond, txt, n_txt, table, x,
+                            workspace);
+  if (rc) return rc;
+  const int n_total = n_img + n_cond + n_txt;
+  REQUIRE(ws_bytes >= sample_ws_bytes(n_img, n_total), FLUX3_EWORKSPACE,
+          "workspace %zu < %zu bytes", ws_bytes, sample_ws_bytes(n_img, n_total));
+  if (steps == 0) return FLUX3_OK;
+  char* p = (char*)workspace + stack_ws_bytes(n_total);
+  float* v = (float*)p;
+  bf16* xb = (bf16*)(p + align256((size_t)n_img * 128 * 4));
+  const int n_lat = n_img * 128;
+  launch_euler(x, xb, nullptr, n_lat, 0.f, stream);  // xb = bf16(x)
+  for (int k = 0; k < steps; ++k) {
+    rc = stack_forward_unchecked(w, (const uint16_t*)xb, n_img, cond, n_cond, txt, n_txt, table,
+                                 sigmas[k], sigmas[k + 1], v, workspace, stream);
+    if (rc) return rc;
+    launch_euler(x, k + 1 < steps ? xb : nullptr, v, n_lat, sigmas[k + 1] - sigmas[k], stream);
+  }
+  return check_launch("sample");
 }
 
 int flux3_euler_step(float* x, uint16_t* x_bf16, const float* v, int n, float sigma,

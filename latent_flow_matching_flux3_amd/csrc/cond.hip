@@ -86,13 +86,14 @@ void launch_gemv(const GemvBatch& batch, int nb, int rows, int K, bool silu_x, b
                      accumulate ? 1 : 0);
 }
 
-// x += (sigma_next - sigma) * v; xb = bf16(x).
+// x += (sigma_next - sigma) * v; xb = bf16(x).  v == nullptr: x unchanged,
+// only the bf16 copy is written.
 __global__ void euler_kernel(float* __restrict__ x, bf16* __restrict__ xb,
                              const float* __restrict__ v, int n, float dt) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  const float y = x[i] + dt * v[i];
-  x[i] = y;
+  const float y = v ? x[i] + dt * v[i] : x[i];
+  if (v) x[i] = y;
   if (xb) xb[i] = to_bf16(y);
 }
 

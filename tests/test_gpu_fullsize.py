@@ -4,7 +4,9 @@ that the oracle computes one by one (keys and values from every row).
 
 Workloads: 1024^2 text-to-image (64x64 image + 512 text = 4608 tokens),
 1024^2 image-to-image with one reference (8704 tokens), four references
-(20992 tokens)."""
+(20992 tokens), and the four bars of the blog's tokens-per-call chart
+(4256, 8272, 4336 tokens, and 8800 with the non-square 85x48 grid): text
+lengths that are multiples of 80 and row counts with ragged tiles."""
 import numpy as np
 import pytest
 import torch
@@ -31,9 +33,10 @@ def _sample_rows(lay, k=40, seed=0):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["block_t2i_1024_4608tok", "block_i2i_1024_8704tok", "stack_4ref_1024_20992tok"])
+@pytest.mark.parametrize("name", ["block_t2i_1024_4608tok", "block_i2i_1024_8704tok", "stack_4ref_1024_20992tok"]
+                         + list(syn.PAGE_WORKLOADS))
 def test_block_full_size_sampled(L, name):
-    lay = syn.WORKLOADS[name]
+    lay = syn.WORKLOADS.get(name) or syn.PAGE_WORKLOADS[name]
     n = lay.n_total
     ids = O.build_ids(lay.img_h, lay.img_w, lay.n_txt, lay.refs)
     segs = [0] + [b for _, _, b in lay.segments()]

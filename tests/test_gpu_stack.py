@@ -131,3 +131,87 @@ def test_flow_map_sampler(L):
 
     xr = O.sample_flow_map(velocity, f64(img), steps)
     assert_agree(f64(x), xr, "sampler 4 steps")
+
+
+def _sample_setup(L, lay, seed, n_early, n_single):
+    wts = Weights(L, seed, lay, n_early, n_single)
+    img, cond, txt = _inputs(lay, seed)
+    ids = L.flux3_build_ids(lay.img_h, lay.img_w, lay.n_txt, lay.refs).to("cuda")
+    table = L.flux3_rope_table(ids)
+    return wts, img, cond, txt, table
+
+
+def test_sample_one_call(L):
+    """flux3_sample (the whole loop in one call) on a non-square grid with a
+    reference and an 80-token text: bit-identical to the step-by-step calls,
+    and within tolerance of the oracle's sampler."""
+    lay = syn.Layout(6, 11, 80, [(6, 11)])
+    seed = 310
+    steps = 3
+    wts, img, cond, txt, table = _sample_setup(L, lay, seed, 1, 1)
+    sig = L.flux3_sigmas(steps)
+    cond_d, txt_d = dev(cond), dev(txt)
+    say(f"sample one call n={lay.n_total} steps={steps}")
+    x = dev(img).float()
+    ws = L.workspace(L.flux3_sample_workspace_size(lay.n_img, lay.n_cond, lay.n_txt))
+    L.flux3_sample(wts.model, x, cond_d, txt_d, table, sig, ws)
+    # the same loop through the per-step entry points
+    xs, xb = dev(img).float(), dev(img)
+    v = torch.empty((lay.n_img, 128), dtype=torch.float32, device="cuda")
+    sws = L.workspace(L.flux3_stack_workspace_size(lay.n_img, lay.n_cond, lay.n_txt))
+    s = sig.tolist()
+    for k in range(steps):
+        L.flux3_stack_forward(wts.model, xb, cond_d, txt_d, table, s[k], s[k + 1], v, sws)
+        L.flux3_euler_step(xs, xb, v, s[k], s[k + 1])
+    torch.cuda.synchronize()
+    assert torch.equal(x, xs), "flux3_sample differs from the step-by-step loop"
+
+    def velocity(xx, a, b):
+        return O.stack_forward(wts.W, wts.B, xx, f64(cond), f64(txt), lay.img_h, lay.img_w, lay.refs,
+                               a, b, 1, 1)
+
+    xr = O.sample_flow_map(velocity, f64(img), steps)
+    assert_agree(f64(x), xr, f"sample {steps} steps")
+    # zero steps leave x alone
+    x0 = x.clone()
+    L.flux3_sample(wts.model, x, cond_d, txt_d, table, sig[:1], ws)
+    torch.cuda.synchronize()
+    assert torch.equal(x, x0)
+
+
+def test_sample_graph_replays(L):
+    """flux3_sample captured into one HIP graph: every replay (with eager
+    library work and synchronisations between replays, sharing the
+    workspace) equals the eager call bit for bit."""
+    lay = syn.Layout(4, 4, 8)
+    seed = 320
+    wts, img, _, txt, table = _sample_setup(L, lay, seed, 1, 1)
+    sig = L.flux3_sigmas(4)
+    txt_d = dev(txt)
+    ws = L.workspace(L.flux3_sample_workspace_size(lay.n_img, 0, lay.n_txt))
+    x0 = dev(img).float()
+    xe = x0.clone()
+    say("sample graph: eager")
+    L.flux3_sample(wts.model, xe, None, txt_d, table, sig, ws)
+    torch.cuda.synchronize()
+    xg = x0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        L.flux3_sample(wts.model, xg, None, txt_d, table, sig, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(xg, xe)
+    say("sample graph: capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.flux3_sample(wts.model, xg, None, txt_d, table, sig, ws)
+    for r in range(3):
+        say(f"sample graph: replay {r}")
+        xo = x0.clone()
+        L.flux3_sample(wts.model, xo, None, txt_d, table, sig[:3], ws)  # eager work in between
+        xg.copy_(x0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(xg, xe), f"replay {r} differs from the eager call"

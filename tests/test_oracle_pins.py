@@ -64,6 +64,17 @@ def test_tokens_per_call_chart():
     assert O.padded_text_len(1) == 80 and O.padded_text_len(81) == 160
 
 
+def test_page_workloads_match_the_chart():
+    """The seeded page workloads reproduce the chart's four bars exactly."""
+    g = _load("page_facts.json")["tokens_per_call"]
+    lays = list(syn.PAGE_WORKLOADS.values())
+    assert len(lays) == len(g["cases"])
+    for lay, case in zip(lays, g["cases"]):
+        assert (lay.img_h, lay.img_w) == O.token_grid(*case["output_px"])
+        assert lay.refs == [O.token_grid(*r) for r in case["refs_px"]]
+        assert lay.n_total == case["total"] and lay.n_txt % g["text_pad_multiple"] == 0
+
+
 def test_schedule_facts():
     g = _load("page_facts.json")["schedule"]
     s = O.sigmas(g["steps"], g["alpha"])
