@@ -151,12 +151,7 @@ void launch_gemm(const GemmArgs& g, hipStream_t st) {
     }
   }
   if (g.N % 256 == 0 && big_tiles >= 192) {
-    // Long products (the block's output projection, K = 12288) keep more
-    // slices in flight: five 32-wide slices instead of two 64-wide ones.
-    if (g.K >= 8192)
-      run_ring<256, 256, 2, 2, 32, 5, 1>(g, st);
-    else
-      run_ring<256, 256, 2, 2, 64, 2, 1>(g, st);
+    run_ring<256, 256, 2, 2, 32, 5, 1>(g, st);
   } else if (g.N % 128 == 0) {
     run_regs<128, 128, 2, 2>(g, st);
   } else {
@@ -169,7 +164,7 @@ int launch_gemm_variant(const GemmArgs& g, int cfg, hipStream_t st) {
   switch (cfg) {
     case 0: run_regs<256, 256, 2, 4>(g, st); return 0;
     case 1: run_regs<128, 128, 2, 2>(g, st); return 0;
-    case 9: run_ring<256, 256, 2, 2, 64, 2, 1>(g, st); return 0;
+    case 9: run_ring<256, 256, 2, 2, 32, 4, 1>(g, st); return 0;
     case 11: run_ring<256, 256, 2, 2, 32, 5, 1>(g, st); return 0;
   }
   return -1;

@@ -18,6 +18,8 @@
 // the 256-byte bank line.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -429,18 +431,18 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  // Load addresses: a uniform tile base (scalar registers) plus a 32-bit
-  // per-lane byte offset.  A lane's offset inside a KiB block depends only on
-  // the block's parity (the swizzle) and, for A, on the clamp of rows past
-  // M-1 in the last tile row, so A keeps one offset per block and B one per
-  // parity.
-  static_assert(B_BLK % 2 == 0, "block parity fixed per B load");
+  // Load addresses: a uniform base (scalar registers: the tile's origin plus
+  // the k offset of the slice) plus a 32-bit per-lane byte offset per KiB
+  // block.  A lane's offset inside a block depends only on the block's row
+  // (its swizzle) and, for A, on the clamp of rows past M-1 in the last tile
+  // row, so the B offsets are fixed and the A offsets change with the tile.
   const int sub_row = lane / CPR;
-  unsigned voff_a[A_BLK], voff_b[2];
+  unsigned voff_a[A_BLK], voff_b[B_BLK];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int chunk = (lane % CPR) ^ ((4 * p + sub_row / Lay::RPL) % CPR);
-    voff_b[p] = (unsigned)(sub_row * g.ldb * 2 + chunk * 16);
+  for (int q = 0; q < B_BLK; ++q) {
+    const int row = (wave * B_BLK + q) * Lay::RPB + sub_row;
+    const int chunk = (lane % CPR) ^ Lay::swz(row);
+    voff_b[q] = (unsigned)(row * g.ldb * 2 + chunk * 16);
   }
   const char* a_tile;
   const char* b_tile;
@@ -459,17 +461,30 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
       voff_a[q] = (unsigned)((min(m0 + row, g.M - 1) - m0) * g.lda * 2 + chunk * 16);
     }
   };
-  auto load_one = [&](int q, int slot, int koff) {
-    if (q < A_BLK) {
-      const int blk = wave * A_BLK + q;
-      __builtin_amdgcn_global_load_lds((const gmem_void_t*)(a_tile + koff * 2 + voff_a[q]),
-                                       (lds_void_t*)(lds + slot * STAGE + blk * 64), 16, 0, 0);
-    } else {
-      const int blk = wave * B_BLK + (q - A_BLK);
-      __builtin_amdgcn_global_load_lds(
-          (const gmem_void_t*)(b_tile + ((size_t)blk * Lay::RPB * g.ldb + koff) * 2 + voff_b[q & 1]),
-          (lds_void_t*)(lds + slot * STAGE + (BM / Lay::RPB + blk) * 64), 16, 0, 0);
-    }
+  // One KiB of a slice into LDS from the open refill (sources r_a / r_b,
+  // this wave's part of LDS buffer r_dst): each lane lands 16 bytes at
+  // m0 + 16 * lane; writing m0 needs one wait state before the load reads
+  // it.  Issued as inline assembly: the compiler would otherwise treat the
+  // LDS write as possibly aliasing every fragment read that follows it and
+  // wait for all loads in flight before each of them.  The ring's explicit
+  // vmcnt waits and barriers order these loads against the reads; they have
+  // no register results.
+  const unsigned lds_base = (unsigned)(size_t)(lds_void_t*)lds;
+  const char* r_a = nullptr;
+  const char* r_b = nullptr;
+  unsigned r_dst = 0;
+  auto open_refill = [&](int slot, int koff) {
+    r_a = a_tile + koff * 2;
+    r_b = b_tile + koff * 2;
+    r_dst = lds_base + (unsigned)(slot * STAGE) * 16u;
+  };
+  auto load_one = [&](int q) __attribute__((always_inline)) {
+    const bool is_a = q < A_BLK;
+    const int blk = is_a ? wave * A_BLK + q : BM / Lay::RPB + wave * B_BLK + (q - A_BLK);
+    const unsigned dst = r_dst + (unsigned)blk * 1024u;
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(is_a ? voff_a[q] : voff_b[q - A_BLK]), "s"(is_a ? r_a : r_b), "s"(dst)
+                 : "m0");
   };
   // Load cursor: tile ld_i, slice ld_kt.  Past the last slice it stays there:
   // every refill still issues PER loads (the final slice again, into buffers
@@ -512,35 +527,50 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     for (int j = 0; j < T::FN; ++j) bfr[p][j] = lds[buf + b_base + j * 32 * CPR + ch];
   };
 
+  // Refill scheme.  The barrier before the last k step of slice t (every
+  // wave has read all of slice t, slice t+1 has landed) opens the refill of
+  // slice t's buffer with the slice STAGES ahead.  Its PER loads are spread
+  // over the next KSTEPS k steps (the last step of slice t and the first
+  // KSTEPS-1 steps of slice t+1), LPS per step, each one issued right after
+  // an MFMA: a 64-lane load holds up the wave's instruction issue for a
+  // while, and behind a just-issued MFMA that time is mostly hidden (all
+  // PER loads in one step cost ~20% of the MFMA rate, spread this way ~9%).
+  // So one refill is issued between consecutive barriers, and the slice a
+  // barrier waits for had STAGES-2 refills issued after it.
+  constexpr int LPS = PER / KSTEPS;
+  static_assert(T::FM == 4 && T::FN == 4, "four MFMA segments of four per step");
+  static_assert(PER % KSTEPS == 0 && LPS <= 4, "refill loads per step");
+  static_assert(STAGES >= 3, "a refill spans a barrier");
   static_assert(KSTEPS % 2 == 0, "the next slice's first fragments land in slot 0");
-  auto mfma_step = [&](int p) {
+  // One k step: its 16 MFMAs (fragments P) in four segments.  Each segment
+  // also reads two fragments of the next step (into 1-P), then one load of
+  // the open refill (the first LPS segments).
+  auto step = [&](auto P, int rbuf, int rks, int q0) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
+    const int ch = (2 * rks + lh) ^ sw;
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i)
+    for (int seg = 0; seg < 4; ++seg) {
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j)
-        acc[i][j] = mma(af[p][i], bfr[p][j], acc[i][j]);
-  };
-  // Steps 0 .. KSTEPS-2 of the slice in buffer `cur`.  The fragments of the
-  // current step were read a whole step earlier; waiting for them before
-  // issuing the next reads keeps at most FM + FN reads outstanding (lgkmcnt
-  // only counts to 15) and costs nothing.
-  static_assert(NMF % (T::FM + T::FN) == 0, "MFMAs per fragment read");
-  auto inner_steps = [&](int cur) {
-#pragma unroll
-    for (int ks = 0; ks + 1 < KSTEPS; ++ks) {
-      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
-      read_frags(cur, ks + 1, (ks & 1) ^ 1);
-      mfma_step(ks & 1);
-      // One fragment read, then its share of the MFMAs, so the read burst
-      // never leaves the MFMA pipe without work.
-#pragma unroll
-      for (int q = 0; q < T::FM + T::FN; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, NMF / (T::FM + T::FN), 0);  // MFMA
+      for (int f = 2 * seg; f < 2 * seg + 2; ++f) {
+        if (f < T::FM) af[p ^ 1][f] = lds[rbuf + a_base + f * 32 * CPR + ch];
+        else bfr[p ^ 1][f - T::FM] = lds[rbuf + b_base + (f - T::FM) * 32 * CPR + ch];
       }
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) acc[seg][j] = mma(af[p][seg], bfr[p][j], acc[seg][j]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (seg < LPS) load_one(q0 + seg);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  constexpr int pl = (KSTEPS - 1) & 1;  // fragment slot of the last step (1)
+  using PL = std::integral_constant<int, pl>;
+
   // Output origin of this wave in the tile being computed, found before the
   // tile's main loop (scalar registers), so nothing but the epilogue itself
   // runs between the last MFMA and the stores.
@@ -553,47 +583,54 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   };
   auto store_tile = [&]() { epilogue<T, EPI>(g, acc, out_row, out_col); };
 
+  // Prologue: slices 0 .. STAGES-2, then the refill of the last buffer is
+  // opened as if at a barrier (its first LPS loads now, the rest in the
+  // first steps of slice 0), so every k step carries LPS loads.
   set_src(0);
 #pragma unroll
-  for (int s = 0; s < STAGES; ++s) {
+  for (int s = 0; s + 1 < STAGES; ++s) {
+    open_refill(s, ld_kt * BK);
 #pragma unroll
-    for (int q = 0; q < PER; ++q) load_one(q, s, ld_kt * BK);
+    for (int q = 0; q < PER; ++q) load_one(q);
     advance_load();
   }
-  wait_vmcnt<(STAGES - 1) * PER>();
+  open_refill(STAGES - 1, ld_kt * BK);
+#pragma unroll
+  for (int q = 0; q < LPS; ++q) load_one(q);
+  wait_vmcnt<(STAGES - 2) * PER + LPS>();
   __syncthreads();
   // Nothing but LDS reads may be pending on lgkmcnt inside the loop (a pending
   // scalar load would force full waits), so settle the scalar loads here.
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
   read_frags(0, 0, 0);
 
-  constexpr int pl = (KSTEPS - 1) & 1;  // fragment slot of the last step (1)
   int slot = 0;
   for (int ti = 0; ti < walk.count; ++ti) {
     set_out(ti);
     for (int kt = 0; kt < KT; ++kt) {
-      inner_steps(slot * STAGE);
-      // The next slice landed for this wave (STAGES-2 slices issued after
+      // Steps 0 .. KSTEPS-2.  The fragments of a step were read a whole step
+      // earlier; waiting for them before issuing the next reads keeps at most
+      // FM + FN reads outstanding (lgkmcnt only counts to 15) and costs
+      // nothing.
+#pragma unroll
+      for (int ks = 0; ks + 1 < KSTEPS; ++ks) {
+        __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
+        if (ks & 1) step(P1{}, slot * STAGE, ks + 1, LPS * (ks + 1));
+        else step(P0{}, slot * STAGE, ks + 1, LPS * (ks + 1));
+      }
+      advance_load();  // the open refill is complete
+      // The next slice landed for this wave (STAGES-2 refills issued after
       // it), and after the barrier for every wave; everyone has read this
       // slice.
       wait_vmcnt<(STAGES - 2) * PER>();
       __syncthreads();
       const int next = slot + 1 == STAGES ? 0 : slot + 1;
-      // At a tile end the next slice's first fragments are read after the
-      // epilogue, so they are not live across it.
-      if (kt + 1 < KT) read_frags(next * STAGE, 0, pl ^ 1);
-      const int koff = ld_kt * BK;
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::FN; ++j) {
-          acc[i][j] = mma(af[pl][i], bfr[pl][j], acc[i][j]);
-#pragma unroll
-          for (int q = i * T::FN + j; q < PER; q += NMF) load_one(q, slot, koff);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-      advance_load();
+      open_refill(slot, ld_kt * BK);
+      // Last step, with the reads of the next slice's first fragments (the
+      // ring streams across tiles, so that slice has landed).  At a tile end
+      // they are read again after the epilogue, so nothing read here is
+      // live across it.
+      step(PL{}, next * STAGE, 0, 0);
       slot = next;
     }
     store_tile();
