@@ -59,7 +59,22 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short short4_t;
 __device__ __forceinline__ int k_phys(int row, int c) { return row * 16 + (c ^ (row & 15)); }
 __device__ __forceinline__ int v_phys(int row, int c) { return row * 16 + (c ^ (4 * (row & 3))); }
 
-__device__ __forceinline__ float half_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
+// max(x, x of lane ^ 32) with v_permlane32_swap (VALU, no LDS round trip).
+// After the swap a = [x_lo | x_lo] and b = [x_hi | x_hi].  Written as one asm
+// block: this compiler's folding of the builtin with two copies of the same
+// value drops half of the result.  The nops give the cross-lane read of the
+// just-written copy, and the max's read of the swap results, their wait states.
+__device__ __forceinline__ float half_max(float x) {
+  float a = x, b;
+  asm volatile(
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %1\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "+v"(a), "=&v"(b));
+  return a;
+}
 __device__ __forceinline__ float half_sum(float x) { return x + __shfl_xor(x, 32, 64); }
 
 template <int N>
@@ -202,9 +217,10 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
       }
   };
 
-  // Softmax of one tile: returns the probabilities as bf16 B operands and
-  // updates m_run / l_run / oacc.
-  auto softmax = [&](floatx16& s, int key0, bf16x8 (&pf)[2]) {
+  // Softmax of tile t, first part: mask keys past the end, row max, and the
+  // (rare) move of the reference max with the rescale of O and l.  Both tests
+  // are wave-uniform branches, kept ahead of the branch-free part below.
+  auto softmax_head = [&](floatx16& s, int key0) {
     if (key0 + kBKV > n) {  // keys past the end get probability 0
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -230,14 +246,6 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
     }
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m_run));
-      psum += p;
-      pf[r >> 3][r & 7] = to_bf16(p);
-    }
-    l_run += psum;
   };
 
   const int ntiles = (n + kBKV - 1) / kBKV;
@@ -261,8 +269,27 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
   // all of its keys, so it adds nothing; an odd tile count runs one fully
   // masked step.
   auto step = [&](int t, floatx16& cur, floatx16& nxt) {
-    scores((t + 1) % kNBuf, nxt);
-    softmax(cur, t * kBKV, pf);
+    // K fragments of tile t+1, read ahead of the softmax's branches.
+    const int ns = (t + 1) % kNBuf;
+    bf16x8 kf[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) kf[st] = ks_lds[ns][k_phys(lr, 2 * st + lh)];
+    softmax_head(cur, t * kBKV);
+    // One branch-free region: the score MFMAs of tile t+1 with the
+    // exponentials of tile t between them (two per MFMA).
+    const floatx16 zero = {};
+    float psum = 0.f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], st == 0 ? zero : nxt, 0, 0, 0);
+#pragma unroll
+      for (int r = 2 * st; r < 2 * st + 2; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(cur[r], scale_log2, -m_run));
+        psum += p;
+        pf[r >> 3][r & 7] = to_bf16(p);
+      }
+    }
+    l_run += psum;
     pv(t % kNBuf, pf);
   };
   for (int t = 0; t < ntiles; t += 2) {
