@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the stack step at the longest sequence (10 references, 49,136 tokens)")
     ap.add_argument("--no-sampler-loop", action="store_true",
                     help="skip the timing of the 16-step loop as one call (eager and graph)")
     ap.add_argument("--only", default=None,
@@ -188,6 +190,31 @@ def sampler_loop(L, torch, model, img, txt, table, n_img: int, n_txt: int, steps
     return {"tokens": n, "steps": steps, "eager_ms_per_image": round(eager, 3),
             "graph_ms_per_image": round(graph_ms, 3), "graph_steps_per_s": round(steps * 1e3 / graph_ms, 2),
             "graph_tflops": round(steps * stack_flops(n_img, 0, n_txt) / (graph_ms * 1e-3) / 1e12, 1)}
+
+
+def long_step(L, torch, syn, model, seed: int, steps: int = 2):
+    """One flow-map step of the whole stack at the longest sequence the pages
+    allow (1024^2 image, ten 1024^2 references, 4080 text tokens), timed with
+    HIP events over `steps` steps after one warm-up."""
+    name = "stack_10ref_1024_49136tok"
+    lay = syn.LONG_WORKLOADS[name]
+    img = syn.latents(seed + 5, lay.n_img).to("cuda")
+    cond = syn.latents(seed + 6, lay.n_cond, "cond").to("cuda")
+    txt = syn.text_features(seed + 7, lay.n_txt).to("cuda")
+    table = L.flux3_rope_table(L.flux3_build_ids(lay.img_h, lay.img_w, lay.n_txt, lay.refs).to("cuda"))
+    ws = L.workspace(L.flux3_stack_workspace_size(lay.n_img, lay.n_cond, lay.n_txt))
+    v = torch.empty((lay.n_img, 128), dtype=torch.float32, device="cuda")
+    sig = L.flux3_sigmas(16).tolist()
+
+    def run():
+        L.flux3_stack_forward(model, img, cond, txt, table, sig[0], sig[1], v, ws)
+
+    ms = event_time_ms(torch, run, steps)
+    assert torch.isfinite(v).all().item(), "non-finite velocity"
+    flops = stack_flops(lay.n_img, lay.n_cond, lay.n_txt)
+    del ws
+    return {"workload": name, "tokens": lay.n_total, "steps": steps, "ms_per_step": round(ms, 2),
+            "tflop_per_step": round(flops / 1e12, 1), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
 
 
 def cpu_baseline(seed: int):
@@ -331,6 +358,11 @@ def main():
         s_table = L.flux3_rope_table(L.flux3_build_ids(small.img_h, small.img_w, small.n_txt).to("cuda"))
         loops["96tok"] = sampler_loop(L, torch, model, s_img, s_txt, s_table, small.n_img, small.n_txt, 16)
 
+    long_ctx = None
+    if not args.no_long:
+        print("[bench] stack step at the longest sequence (49,136 tokens)", file=sys.stderr, flush=True)
+        long_ctx = long_step(L, torch, syn, model, args.seed)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle, one block)", file=sys.stderr, flush=True)
@@ -359,6 +391,7 @@ def main():
         "roofline": roof,
         "kernels": per_kernel,
         "sampler_loop": loops,
+        "long_context": long_ctx,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

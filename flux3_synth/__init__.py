@@ -206,6 +206,12 @@ PAGE_WORKLOADS = {
     "block_layout_i2i_1360x768_page_8800tok": Layout(48, 85, 640, [(48, 85)]),
 }
 
+# The longest sequence the pages allow: a 1024^2 image, ten 1024^2 references
+# and the text at its cap (the largest multiple of 80 not above 4096).
+LONG_WORKLOADS = {
+    "stack_10ref_1024_49136tok": Layout(64, 64, 4080, [(64, 64)] * 10),
+}
+
 
 def block_activations(seed: int, n: int) -> torch.Tensor:
     """Residual-stream input of one block, N(0,1) bf16 [n, 3072]."""

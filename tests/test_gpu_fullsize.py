@@ -6,7 +6,8 @@ Workloads: 1024^2 text-to-image (64x64 image + 512 text = 4608 tokens),
 1024^2 image-to-image with one reference (8704 tokens), four references
 (20992 tokens), and the four bars of the blog's tokens-per-call chart
 (4256, 8272, 4336 tokens, and 8800 with the non-square 85x48 grid): text
-lengths that are multiples of 80 and row counts with ragged tiles."""
+lengths that are multiples of 80 and row counts with ragged tiles; and the
+longest sequence the pages allow (ten references, 4080 text tokens: 49,136)."""
 import numpy as np
 import pytest
 import torch
@@ -34,9 +35,9 @@ def _sample_rows(lay, k=40, seed=0):
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["block_t2i_1024_4608tok", "block_i2i_1024_8704tok", "stack_4ref_1024_20992tok"]
-                         + list(syn.PAGE_WORKLOADS))
+                         + list(syn.PAGE_WORKLOADS) + list(syn.LONG_WORKLOADS))
 def test_block_full_size_sampled(L, name):
-    lay = syn.WORKLOADS.get(name) or syn.PAGE_WORKLOADS[name]
+    lay = syn.WORKLOADS.get(name) or syn.PAGE_WORKLOADS.get(name) or syn.LONG_WORKLOADS[name]
     n = lay.n_total
     ids = O.build_ids(lay.img_h, lay.img_w, lay.n_txt, lay.refs)
     segs = [0] + [b for _, _, b in lay.segments()]

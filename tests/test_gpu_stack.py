@@ -73,6 +73,7 @@ def _gpu_stack(L, wts, lay, img, cond, txt, sigma, sigma_next):
     (syn.Layout(4, 4, 8), 1, 2),
     (syn.Layout(3, 5, 11, [(2, 3), (4, 2)]), 2, 1),
     (syn.Layout(12, 12, 40, [(12, 12)]), 1, 1),
+    (syn.Layout(3, 4, 80, [(2, 3)] * 10), 1, 1),   # ten references: l = -1 .. -10
 ])
 def test_stack_reduced_depth(L, lay, n_early, n_single):
     seed = 100 + lay.n_total

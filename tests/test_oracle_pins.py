@@ -475,3 +475,19 @@ def test_stack_uses_each_modulation_where_the_pages_say():
     v2 = O.final_layer(s[0], vecs["image"], W("final_layer.image.adaLN_modulation.1.weight"),
                        W("final_layer.image.linear.weight"))
     np.testing.assert_array_equal(v, v2)
+
+
+def test_longest_sequence():
+    """Ten 1024^2 references and the longest padded text: 49,136 tokens; the
+    references take l = -1 .. -10."""
+    g = _load("page_facts.json")["longest_sequence"]
+    lay = syn.LONG_WORKLOADS["stack_10ref_1024_49136tok"]
+    h, w = O.token_grid(1024, 1024)
+    assert lay.refs == [(h, w)] * g["max_refs"] and (lay.img_h, lay.img_w) == (h, w)
+    cap = g["text_max_tokens"] // g["text_pad_multiple"] * g["text_pad_multiple"]
+    assert lay.n_txt == cap == O.padded_text_len(cap) and O.padded_text_len(cap + 1) > g["text_max_tokens"]
+    ids = O.build_ids(lay.img_h, lay.img_w, lay.n_txt, lay.refs)
+    assert len(ids) == lay.n_total == 49136
+    l_axis = ids[lay.n_img:lay.n_img + lay.n_cond, 3]
+    assert sorted(set(l_axis.tolist())) == [-float(k) for k in range(10, 0, -1)]
+    assert (ids[lay.n_img + lay.n_cond:, 3] == range(lay.n_txt)).all()
