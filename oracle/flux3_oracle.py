@@ -368,6 +368,31 @@ def sample_flow_map(velocity, x: np.ndarray, steps: int = 16) -> np.ndarray:
     return x
 
 
+BASE_STEPS = 50       # base checkpoint ([issue] Sampling)
+CFG_GUIDANCE = 3.5    # base checkpoint's guidance scale ([issue] Sampling)
+
+
+def cfg_velocity(v_uncond: np.ndarray, v_cond: np.ndarray, guidance: float) -> np.ndarray:
+    """Classifier-free guidance of the base checkpoint's two-sample pack
+    [empty prompt, prompt] ([issue] Sampling, "CFG 3.5"): the unconditional
+    velocity moved `guidance` times along the difference to the conditional
+    one (R13: the usual guidance formula; the pages give only the scale)."""
+    return v_uncond + guidance * (v_cond - v_uncond)
+
+
+def sample_base_cfg(velocity, x: np.ndarray, steps: int = BASE_STEPS,
+                    guidance: float = CFG_GUIDANCE) -> np.ndarray:
+    """Base-checkpoint sampler ([issue] Sampling): the same shifted schedule and
+    Euler update as the flow map, but each step evaluates the model (timestep
+    sigma_k, no ref_time_in) on both samples of the pack and guides.
+    velocity(x, sigma, sample) -> v, sample 0 = empty prompt, 1 = prompt."""
+    s = sigmas(steps)
+    for k in range(steps):
+        v = cfg_velocity(velocity(x, s[k], 0), velocity(x, s[k], 1), guidance)
+        x = x + (s[k + 1] - s[k]) * v
+    return x
+
+
 def euler_update(x: np.ndarray, v: np.ndarray, sigma: float, sigma_next: float) -> np.ndarray:
     """One sampler update x + (sigma_next - sigma) v ([issue] Sampling)."""
     return x + (sigma_next - sigma) * v

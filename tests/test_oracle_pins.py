@@ -388,6 +388,44 @@ def test_sampler_closed_forms():
     assert calls == [(s4, s5) for s4, s5 in zip(O.sigmas(4)[:-1], O.sigmas(4)[1:])]
 
 
+def test_base_cfg_sampler_special_cases():
+    """Guidance 1 is the conditional sampler alone, guidance 0 the
+    unconditional one, equal samples make guidance irrelevant, and linear
+    velocities have a product closed form; the model sees sigma_k only."""
+    x0 = np.array([1.5, -0.5, 2.0])
+    vu = lambda x, s: -x
+    vc = lambda x, s: 0.5 * x + 1.0
+
+    def vel(x, s, i):
+        return vu(x, s) if i == 0 else vc(x, s)
+
+    def plain(v, steps):  # Euler with one velocity
+        sg = O.sigmas(steps)
+        x = x0
+        for k in range(steps):
+            x = x + (sg[k + 1] - sg[k]) * v(x, sg[k])
+        return x
+
+    np.testing.assert_allclose(O.sample_base_cfg(vel, x0, 7, 1.0), plain(vc, 7), rtol=1e-12)
+    np.testing.assert_allclose(O.sample_base_cfg(vel, x0, 7, 0.0), plain(vu, 7), rtol=1e-12)
+    same = lambda x, s, i: vc(x, s)
+    np.testing.assert_allclose(O.sample_base_cfg(same, x0, 5, 3.5), O.sample_base_cfg(same, x0, 5, -2.0),
+                               rtol=1e-12)
+    # guided velocity g*vc + (1-g)*vu = (0.5 g - (1 - g)) x + g: affine steps
+    g, steps = 3.5, 50
+    sg = O.sigmas(steps)
+    a, b = 0.5 * g - (1.0 - g), g
+    x = x0.copy()
+    for k in range(steps):
+        d = sg[k + 1] - sg[k]
+        x = (1.0 + d * a) * x + d * b
+    np.testing.assert_allclose(O.sample_base_cfg(vel, x0), x, rtol=1e-12)
+    calls = []
+    O.sample_base_cfg(lambda x, s, i: calls.append((s, i)) or 0 * x, x0, 3)
+    assert calls == [(s3, i) for s3 in O.sigmas(3)[:-1] for i in (0, 1)]
+    assert O.BASE_STEPS == 50 and O.CFG_GUIDANCE == 3.5
+
+
 def _stack_case(seed, refs, n_early, n_single):
     lay = syn.Layout(2, 3, 5, list(refs))
     W = _global_W(seed)
