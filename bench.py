@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cfg", action="store_true",
+                    help="skip the base checkpoint's guided 50-step sampling")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the stack step at the longest sequence (10 references, 49,136 tokens)")
     ap.add_argument("--no-sampler-loop", action="store_true",
@@ -190,6 +192,55 @@ def sampler_loop(L, torch, model, img, txt, table, n_img: int, n_txt: int, steps
     return {"tokens": n, "steps": steps, "eager_ms_per_image": round(eager, 3),
             "graph_ms_per_image": round(graph_ms, 3), "graph_steps_per_s": round(steps * 1e3 / graph_ms, 2),
             "graph_tflops": round(steps * stack_flops(n_img, 0, n_txt) / (graph_ms * 1e-3) / 1e12, 1)}
+
+
+def cfg_flops(n_img: int, n_t0: int, n_t1: int, n_early: int = 5, n_single: int = 28) -> float:
+    """Algorithmic work of one guided step on the pack (no references): the
+    image stream's embedding and stage 1 once, both texts, stage 2 on both
+    samples (GEMMs on all rows, attention within each sample), final layer on
+    both image blocks, conditioning once."""
+    gemm_row = 2.0 * (4 * HIDDEN * HIDDEN + 3 * HIDDEN * MLP)   # per row per block
+    att = lambda n: 4.0 * n * n * HIDDEN
+    n0, n1 = n_img + n_t0, n_img + n_t1
+    f = 2.0 * n_img * 128 * HIDDEN + 2.0 * (n_t0 + n_t1) * 20480 * HIDDEN
+    f += n_early * (gemm_row * (n_img + n_t0 + n_t1) + att(n_img) + att(n_t0) + att(n_t1))
+    f += n_single * (gemm_row * (n0 + n1) + att(n0) + att(n1))
+    f += 2.0 * 2 * n_img * HIDDEN * 128
+    f += 2.0 * (HIDDEN * 256 + HIDDEN * HIDDEN) * 2 + 2.0 * 3 * HIDDEN * HIDDEN * 2 * 2 + 2.0 * 2 * HIDDEN * HIDDEN
+    return f
+
+
+def cfg_base(L, torch, syn, model, seed: int):
+    """The base checkpoint's guided sampling: pack [empty prompt (80 tokens),
+    prompt (512 tokens)] on a 1024^2 image, guidance 3.5, 50 steps, the same
+    weights without ref_time_in.  One guided step timed with HIP events (3
+    after a warm-up), then the 50-step loop as one flux3_sample_cfg call."""
+    base = L.ModelWeights({k: t for k, t in model.glob.items() if not k.startswith("ref_time_in.")},
+                          model.early, model.single)
+    n_img, n_t0, n_t1, g, steps = 4096, 80, 512, 3.5, 50
+    img = syn.latents(seed + 8, n_img).to("cuda")
+    txt0 = syn.text_features(seed + 9, n_t0).to("cuda")
+    txt1 = syn.text_features(seed + 10, n_t1).to("cuda")
+    table = L.flux3_rope_table(L.flux3_build_ids_cfg(64, 64, n_t0, n_t1).to("cuda"))
+    ws = L.workspace(L.flux3_sample_cfg_workspace_size(n_img, 0, n_t0, n_t1))
+    v = torch.empty((n_img, 128), dtype=torch.float32, device="cuda")
+    sig = L.flux3_sigmas(steps)
+    s0 = float(sig[0])
+    ms = event_time_ms(torch, lambda: L.flux3_stack_forward_cfg(base, img, None, txt0, txt1, table, s0, 0.0,
+                                                                g, v, ws), 3)
+    x = img.float().contiguous()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    L.flux3_sample_cfg(base, x, None, txt0, txt1, table, sig, g, ws)
+    e1.record(st)
+    e1.synchronize()
+    loop_ms = e0.elapsed_time(e1)
+    assert torch.isfinite(x).all().item(), "non-finite sample"
+    f = cfg_flops(n_img, n_t0, n_t1)
+    return {"workload": "cfg_base_t2i_1024_pack_80_512tok", "rows": 2 * n_img + n_t0 + n_t1, "guidance": g,
+            "ms_per_step": round(ms, 2), "tflop_per_step": round(f / 1e12, 2),
+            "tflops": round(f / (ms * 1e-3) / 1e12, 1), "steps": steps, "image_s": round(loop_ms / 1e3, 3)}
 
 
 def long_step(L, torch, syn, model, seed: int, steps: int = 2):
@@ -358,6 +409,11 @@ def main():
         s_table = L.flux3_rope_table(L.flux3_build_ids(small.img_h, small.img_w, small.n_txt).to("cuda"))
         loops["96tok"] = sampler_loop(L, torch, model, s_img, s_txt, s_table, small.n_img, small.n_txt, 16)
 
+    cfg = None
+    if not args.no_cfg:
+        print("[bench] base checkpoint: guided pack, 50-step loop", file=sys.stderr, flush=True)
+        cfg = cfg_base(L, torch, syn, model, args.seed)
+
     long_ctx = None
     if not args.no_long:
         print("[bench] stack step at the longest sequence (49,136 tokens)", file=sys.stderr, flush=True)
@@ -391,6 +447,7 @@ def main():
         "roofline": roof,
         "kernels": per_kernel,
         "sampler_loop": loops,
+        "cfg_base": cfg,
         "long_context": long_ctx,
         "cpu_baseline": cpu,
     }

@@ -305,6 +305,50 @@ int flux3_sample(const flux3_model_weights* w, float* x, int n_img, const uint16
                  const float* sigmas, int steps, void* workspace, size_t ws_bytes,
                  hipStream_t stream);
 
+/* ---- base checkpoint: guided sampling on a two-sample pack ----------------------
+ * [issue] "Sampling": the base checkpoint runs 50 steps of the same Euler update
+ * with classifier-free guidance 3.5 on a pack of two samples, [empty prompt,
+ * prompt], and has no ref_time_in.  Guidance: v = v0 + g (v1 - v0), sample 0
+ * the empty prompt, sample 1 the prompt (the usual formula; the pages give the
+ * scale only).  Both samples share the image latents and references.
+ *
+ * flux3_build_ids_cfg: ids (as flux3_build_ids) of the packed rows, host only:
+ *   sample 0: image | references | text 0 (indices 0 ..),
+ *   sample 1: text 1 (indices 0 ..) | image | references.
+ *   ids: host [n][4] fp32 or NULL (then only *n_out is set). */
+int flux3_build_ids_cfg(int img_h, int img_w, int n_refs, const int* ref_hw, int n_txt0, int n_txt1,
+                        float* ids, int* n_out);
+
+/* flux3_stack_forward_cfg: the guided velocity of one step.  The image and
+ * reference streams go through stage 1 once (they are the same for both
+ * samples); the texts run side by side, each attending to itself; stage 2 runs
+ * both samples in one pass, each attending within itself; the final layer
+ * gives v0 and v1, and v = v0 + guidance (v1 - v0).
+ *   w        : model weights; ref_time_in NULL for the base checkpoint (if
+ *              given, ref_time_in(emb(sigma_next)) is added as in the flow map)
+ *   img      : device [n_img][128] bf16;  cond: device [n_cond][128] or NULL
+ *   txt0/txt1: device [n_txt][20480] bf16 (empty prompt / prompt)
+ *   table    : device rope table of the flux3_build_ids_cfg ids
+ *   v        : device output [n_img][128] fp32
+ *   workspace: device, >= flux3_stack_cfg_workspace_size(...) */
+size_t flux3_stack_cfg_workspace_size(int n_img, int n_cond, int n_txt0, int n_txt1);
+int flux3_stack_forward_cfg(const flux3_model_weights* w, const uint16_t* img, int n_img,
+                            const uint16_t* cond, int n_cond, const uint16_t* txt0, int n_txt0,
+                            const uint16_t* txt1, int n_txt1, const float* table, float sigma,
+                            float sigma_next, float guidance, float* v, void* workspace,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* flux3_sample_cfg: the whole guided loop in one call: for k < steps,
+ * v = flux3_stack_forward_cfg(bf16(x), sigmas[k], sigmas[k+1], guidance),
+ * x <- x + (sigmas[k+1] - sigmas[k]) v.  As flux3_sample: no host
+ * synchronisation, no allocation, capturable into one HIP graph.
+ *   x: device [n_img][128] fp32 in/out; sigmas: host [steps+1] fp32. */
+size_t flux3_sample_cfg_workspace_size(int n_img, int n_cond, int n_txt0, int n_txt1);
+int flux3_sample_cfg(const flux3_model_weights* w, float* x, int n_img, const uint16_t* cond,
+                     int n_cond, const uint16_t* txt0, int n_txt0, const uint16_t* txt1, int n_txt1,
+                     const float* table, const float* sigmas, int steps, float guidance,
+                     void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* flux3_sigmas: the shifted schedule, host only ([issue] "Sampling"):
  * t_k = 1 - k/steps, sigma_k = alpha t_k / (1 + (alpha - 1) t_k), k = 0..steps.
  *   out: host [steps+1] fp32 (computed in fp64). */

@@ -75,6 +75,11 @@ _SIGS = {
     "flux3_stack_forward": (I, [C.POINTER(ModelWeightsC), P, I, P, I, P, I, P, F, F, P, P, S, P]),
     "flux3_sample_workspace_size": (S, [I, I, I]),
     "flux3_sample": (I, [C.POINTER(ModelWeightsC), P, I, P, I, P, I, P, P, I, P, S, P]),
+    "flux3_build_ids_cfg": (I, [I, I, I, P, I, I, P, C.POINTER(I)]),
+    "flux3_stack_cfg_workspace_size": (S, [I, I, I, I]),
+    "flux3_stack_forward_cfg": (I, [C.POINTER(ModelWeightsC), P, I, P, I, P, I, P, I, P, F, F, F, P, P, S, P]),
+    "flux3_sample_cfg_workspace_size": (S, [I, I, I, I]),
+    "flux3_sample_cfg": (I, [C.POINTER(ModelWeightsC), P, I, P, I, P, I, P, I, P, P, I, F, P, S, P]),
     "flux3_euler_step": (I, [P, P, P, I, F, F, P]),
     "flux3_sigmas": (I, [I, C.c_double, P]),
 }
@@ -324,6 +329,49 @@ def flux3_sample(weights: ModelWeights, x, cond, txt, table, sigmas, workspace, 
                               _ptr(txt), n_txt, _ptr(table), sig.data_ptr(), sig.numel() - 1,
                               _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream(stream)))
+    return x
+
+
+def flux3_build_ids_cfg(img_h: int, img_w: int, n_txt0: int, n_txt1: int, refs=()) -> torch.Tensor:
+    """Ids of the guided pack's rows (sample 0: image | refs | text 0, sample 1:
+    text 1 | image | refs), host fp32 [n, 4]."""
+    hw = (I * (2 * len(refs)))(*[int(v) for r in refs for v in r])
+    n = I(0)
+    _check(lib().flux3_build_ids_cfg(img_h, img_w, len(refs), hw, n_txt0, n_txt1, None, C.byref(n)))
+    out = torch.empty((n.value, 4), dtype=torch.float32)
+    _check(lib().flux3_build_ids_cfg(img_h, img_w, len(refs), hw, n_txt0, n_txt1, out.data_ptr(), C.byref(n)))
+    return out
+
+
+def _rows(t):
+    return 0 if t is None else t.shape[0]
+
+
+def flux3_stack_cfg_workspace_size(n_img: int, n_cond: int, n_txt0: int, n_txt1: int) -> int:
+    return lib().flux3_stack_cfg_workspace_size(n_img, n_cond, n_txt0, n_txt1)
+
+
+def flux3_stack_forward_cfg(weights: ModelWeights, img, cond, txt0, txt1, table, sigma, sigma_next,
+                            guidance, v, workspace, stream=None):
+    _check(lib().flux3_stack_forward_cfg(C.byref(weights.c), _ptr(img), img.shape[0], _ptr(cond), _rows(cond),
+                                         _ptr(txt0), _rows(txt0), _ptr(txt1), _rows(txt1), _ptr(table),
+                                         float(sigma), float(sigma_next), float(guidance), _ptr(v), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return v
+
+
+def flux3_sample_cfg_workspace_size(n_img: int, n_cond: int, n_txt0: int, n_txt1: int) -> int:
+    return lib().flux3_sample_cfg_workspace_size(n_img, n_cond, n_txt0, n_txt1)
+
+
+def flux3_sample_cfg(weights: ModelWeights, x, cond, txt0, txt1, table, sigmas, guidance, workspace, stream=None):
+    """x: device [n_img, 128] fp32, updated in place; sigmas: [steps + 1] host values."""
+    _require_dev(x, torch.float32, "x")
+    sig = torch.as_tensor(sigmas, dtype=torch.float32).cpu().contiguous()
+    _check(lib().flux3_sample_cfg(C.byref(weights.c), _ptr(x), x.shape[0], _ptr(cond), _rows(cond),
+                                  _ptr(txt0), _rows(txt0), _ptr(txt1), _rows(txt1), _ptr(table),
+                                  sig.data_ptr(), sig.numel() - 1, float(guidance), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
     return x
 
 

@@ -141,9 +141,11 @@ void out_proj(const bf16* cat, int n, const bf16* w_out, float* x, const SegTabl
 }
 
 // a3..a8 with arguments already checked.
+// attn: row groups that attend only within themselves (the samples of a
+// pack, or two text streams in stage 1); nullptr = all n rows together.
 void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* mod,
                              const flux3_block_weights* w, const float* table, const BlockWs& ws,
-                             hipStream_t st) {
+                             hipStream_t st, const SegTable* attn = nullptr) {
   // a3: h = (1 + scale) LN(x) + shift
   launch_ln_modulate(x, kHidden, ws.xm, kHidden, n, seg, mod, 3 * kHidden, st);
   // a4 + a5: q | k | v into qkv; SwiGLU output into the last 9216 columns of cat
@@ -151,9 +153,15 @@ void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
   // a6: RMSNorm + RoPE on q and k
   launch_qk_norm_rope(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, n, B(w->q_scale),
                       B(w->k_scale), table, st);
-  // a7: attention -> first 3072 columns of cat
-  launch_attention(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, ws.qkv + 2 * kHidden,
-                   3 * kHidden, ws.cat, kWOutCols, n, st);
+  // a7: attention -> first 3072 columns of cat, per row group
+  const int ng = attn ? attn->n : 1;
+  for (int gi = 0; gi < ng; ++gi) {
+    const int r0 = attn ? attn->off[gi] : 0, r1 = attn ? attn->off[gi + 1] : n;
+    if (r1 <= r0) continue;
+    const bf16* q = ws.qkv + (size_t)r0 * 3 * kHidden;
+    launch_attention(q, 3 * kHidden, q + kHidden, 3 * kHidden, q + 2 * kHidden, 3 * kHidden,
+                     ws.cat + (size_t)r0 * kWOutCols, kWOutCols, r1 - r0, st);
+  }
   // a8: gated residual
   out_proj(ws.cat, n, B(w->w_out), x, seg, mod, st, ws.qkv, ws.qkv_bytes);
 }
@@ -726,6 +734,324 @@ int flux3_sigmas(int steps, double alpha, float* out) {
     out[k] = (float)(alpha * t / (1.0 + (alpha - 1.0) * t));
   }
   return FLUX3_OK;
+}
+
+}  // extern "C"
+
+// ---- base checkpoint: the guided two-sample pack ---------------------------------
+//
+// Both samples of the pack [empty prompt, prompt] share the image latents and
+// references, so their image and image_cond streams are identical through
+// stage 1 (those streams attend only to themselves and carry the same
+// modulation): they run once.  Rows of the packed residual stream:
+//   sample 0: image | image_cond | text 0,   sample 1: text 1 | image | image_cond
+// so each sample is one contiguous row range (its attention group in stage 2)
+// and the two text streams are adjacent (one stage-1 call, two groups).
+
+namespace {
+
+struct CfgRows {
+  int n_img, n_cond, n_t0, n_t1;
+  int txt0() const { return n_img + n_cond; }
+  int n0() const { return n_img + n_cond + n_t0; }
+  int img1() const { return n0() + n_t1; }
+  int n() const { return img1() + n_img + n_cond; }
+};
+
+struct CfgWs {
+  float* x;          // [n][3072]
+  float* vec;        // [3][3072]
+  float* mod_early;  // [3][9216]
+  float* mod_seg;    // [5][9216] stage-2 modulation per packed segment
+  float* mod_final;  // [6144]
+  char* time_ws;
+  float* v_pair;     // [2][n_img][128]
+  void* block_ws;
+};
+
+size_t cfg_ws_bytes(const CfgRows& r) {
+  return align256((size_t)r.n() * kHidden * 4) + align256(3 * kHidden * 4) +
+         align256(3 * 3 * kHidden * 4) + align256(5 * 3 * kHidden * 4) + align256(2 * kHidden * 4) +
+         align256(kTimeWsBytes) + align256((size_t)2 * r.n_img * 128 * 4) + block_ws_bytes(r.n());
+}
+
+CfgWs carve_cfg_ws(void* ws, const CfgRows& r) {
+  char* p = (char*)ws;
+  CfgWs s;
+  s.x = (float*)p;
+  p += align256((size_t)r.n() * kHidden * 4);
+  s.vec = (float*)p;
+  p += align256(3 * kHidden * 4);
+  s.mod_early = (float*)p;
+  p += align256(3 * 3 * kHidden * 4);
+  s.mod_seg = (float*)p;
+  p += align256(5 * 3 * kHidden * 4);
+  s.mod_final = (float*)p;
+  p += align256(2 * kHidden * 4);
+  s.time_ws = p;
+  p += align256(kTimeWsBytes);
+  s.v_pair = (float*)p;
+  p += align256((size_t)2 * r.n_img * 128 * 4);
+  s.block_ws = p;
+  return s;
+}
+
+int check_cfg_args(const flux3_model_weights* w, const uint16_t* img, const CfgRows& r,
+                   const uint16_t* cond, const uint16_t* txt0, const uint16_t* txt1,
+                   const float* table, const float* v, const void* ws) {
+  REQUIRE(r.n_t0 >= 0 && r.n_t1 >= 0, FLUX3_EINVAL, "n_txt0=%d n_txt1=%d", r.n_t0, r.n_t1);
+  REQUIRE(r.n_t0 == 0 || (txt0 != nullptr && aligned16(txt0)), FLUX3_EINVAL, "txt0 null or misaligned");
+  REQUIRE(r.n_t1 == 0 || (txt1 != nullptr && aligned16(txt1)), FLUX3_EINVAL, "txt1 null or misaligned");
+  REQUIRE((long)r.n_img * 2 + (long)r.n_cond * 2 + r.n_t0 + r.n_t1 < (1L << 30), FLUX3_EINVAL,
+          "too many tokens");
+  // the shared checks see one text stream of n_t0 + n_t1 rows
+  return check_stack_args(w, img, r.n_img, cond, r.n_cond, r.n_t0 ? txt0 : txt1, r.n_t0 + r.n_t1,
+                          table, v, ws);
+}
+
+// One guided velocity evaluation on checked arguments.
+int stack_cfg_unchecked(const flux3_model_weights* w, const uint16_t* img, const uint16_t* cond,
+                        const uint16_t* txt0, const uint16_t* txt1, const CfgRows& r,
+                        const float* table, float sigma, float sigma_next, float guidance, float* v,
+                        void* workspace, hipStream_t stream) {
+  const int n = r.n();
+  const CfgWs s = carve_cfg_ws(workspace, r);
+  const BlockWs bws = carve_block_ws(s.block_ws, n);
+
+  // Modes present (image, image_cond, txt) and their conditioning.
+  int modes[3], n_modes = 0;
+  modes[n_modes++] = 0;
+  if (r.n_cond > 0) modes[n_modes++] = 1;
+  if (r.n_t0 + r.n_t1 > 0) modes[n_modes++] = 2;
+  int is_image[3];
+  for (int i = 0; i < n_modes; ++i) is_image[i] = modes[i] == 0;
+  int rc = time_vectors_unchecked(w->time_in_w1, w->time_in_w2, w->ref_time_in_w1,
+                                  w->ref_time_in_w2, sigma, sigma_next, is_image, n_modes, s.vec,
+                                  s.time_ws, stream);
+  if (rc) return rc;
+  // Early modulation per mode; single modulation per mode straight into the
+  // first n_modes packed segments (sample 0 holds every mode, in mode order).
+  GemvBatch mb{};
+  for (int i = 0; i < n_modes; ++i) {
+    mb.w[i] = B(w->early_mod[modes[i]]);
+    mb.x[i] = s.vec + (size_t)i * kHidden;
+    mb.y[i] = s.mod_early + (size_t)i * 3 * kHidden;
+    mb.w[n_modes + i] = B(w->single_mod[modes[i]]);
+    mb.x[n_modes + i] = s.vec + (size_t)i * kHidden;
+    mb.y[n_modes + i] = s.mod_seg + (size_t)i * 3 * kHidden;
+  }
+  launch_gemv(mb, 2 * n_modes, 3 * kHidden, kHidden, true, false, stream);
+  GemvBatch fb{};
+  fb.w[0] = B(w->final_ada);
+  fb.x[0] = s.vec;
+  fb.y[0] = s.mod_final;
+  launch_gemv(fb, 1, 2 * kHidden, kHidden, true, false, stream);
+
+  // Stage-2 segments in row order; sample 1's image (and image_cond)
+  // segments reuse the modulation of the same modes.
+  SegTable seg2{};
+  int ns = 0;
+  seg2.off[ns++] = 0;
+  if (r.n_cond > 0) seg2.off[ns++] = r.n_img;
+  if (r.n_t0 + r.n_t1 > 0) seg2.off[ns++] = r.txt0();
+  const int img_seg1 = ns;
+  seg2.off[ns++] = r.img1();
+  if (r.n_cond > 0) seg2.off[ns++] = r.img1() + r.n_img;
+  seg2.off[ns] = n;
+  seg2.n = ns;
+  const size_t mod_bytes = 3 * kHidden * sizeof(float);
+  for (int i = 0; img_seg1 + i < ns; ++i) {
+    const hipError_t e = hipMemcpyAsync(s.mod_seg + (size_t)(img_seg1 + i) * 3 * kHidden,
+                                        s.mod_seg + (size_t)i * 3 * kHidden, mod_bytes,
+                                        hipMemcpyDeviceToDevice, stream);
+    REQUIRE(e == hipSuccess, FLUX3_EHIP, "modulation copy: %s", hipGetErrorString(e));
+  }
+
+  // a9: embeddings (image and references once, both texts).
+  struct Emb { const uint16_t* in; const uint16_t* w; int rows, k, row0; };
+  const Emb embs[4] = {{img, w->emb_in_image, r.n_img, 128, 0},
+                       {cond, w->emb_in_image_cond, r.n_cond, 128, r.n_img},
+                       {txt0, w->txt_in, r.n_t0, 20480, r.txt0()},
+                       {txt1, w->txt_in, r.n_t1, 20480, r.n0()}};
+  for (const Emb& e : embs) {
+    if (e.rows == 0) continue;
+    GemmArgs g{};
+    g.A = B(e.in);
+    g.lda = e.k;
+    g.B = B(e.w);
+    g.ldb = e.k;
+    g.M = e.rows;
+    g.N = kHidden;
+    g.K = e.k;
+    g.epi = GemmEpi::kStoreF32;
+    g.C = s.x + (size_t)e.row0 * kHidden;
+    g.ldc = kHidden;
+    g.split_ws = bws.qkv;  // free until the first block
+    g.split_ws_bytes = bws.qkv_bytes;
+    launch_gemm(g, stream);
+  }
+
+  // a10: stage 1.  Image and references once (sample 0's rows), then both
+  // texts in one call with one attention group each; then sample 1 gets a
+  // copy of the shared streams.
+  SegTable one{};
+  one.n = 1;
+  int mi = 0;
+  {
+    one.off[1] = r.n_img;
+    for (int b = 0; b < w->n_early; ++b)
+      block_forward_unchecked(s.x, r.n_img, one, s.mod_early, &w->early[0][b], table, bws, stream);
+    ++mi;
+  }
+  if (r.n_cond > 0) {
+    one.off[1] = r.n_cond;
+    for (int b = 0; b < w->n_early; ++b)
+      block_forward_unchecked(s.x + (size_t)r.n_img * kHidden, r.n_cond, one,
+                              s.mod_early + (size_t)mi * 3 * kHidden, &w->early[1][b],
+                              table + (size_t)r.n_img * 128, bws, stream);
+    ++mi;
+  }
+  const int nt = r.n_t0 + r.n_t1;
+  if (nt > 0) {
+    one.off[1] = nt;
+    SegTable groups{};
+    groups.off[0] = 0;
+    groups.off[1] = r.n_t0;
+    groups.off[2] = nt;
+    groups.n = 2;
+    for (int b = 0; b < w->n_early; ++b)
+      block_forward_unchecked(s.x + (size_t)r.txt0() * kHidden, nt, one,
+                              s.mod_early + (size_t)mi * 3 * kHidden, &w->early[2][b],
+                              table + (size_t)r.txt0() * 128, bws, stream, &groups);
+  }
+  {
+    const hipError_t e = hipMemcpyAsync(s.x + (size_t)r.img1() * kHidden, s.x,
+                                        (size_t)(r.n_img + r.n_cond) * kHidden * sizeof(float),
+                                        hipMemcpyDeviceToDevice, stream);
+    REQUIRE(e == hipSuccess, FLUX3_EHIP, "stream copy: %s", hipGetErrorString(e));
+  }
+
+  // a11: stage 2 on both samples at once; each sample attends within itself.
+  SegTable samples{};
+  samples.off[0] = 0;
+  samples.off[1] = r.n0();
+  samples.off[2] = n;
+  samples.n = 2;
+  for (int b = 0; b < w->n_single; ++b)
+    block_forward_unchecked(s.x, n, seg2, s.mod_seg, &w->single[b], table, bws, stream, &samples);
+
+  // a12: final layer on both samples' image rows, then guidance.
+  one.off[1] = r.n_img;
+  launch_ln_modulate(s.x, kHidden, bws.xm, kHidden, r.n_img, one, s.mod_final, 2 * kHidden, stream);
+  launch_ln_modulate(s.x + (size_t)r.img1() * kHidden, kHidden, bws.xm + (size_t)r.n_img * kHidden,
+                     kHidden, r.n_img, one, s.mod_final, 2 * kHidden, stream);
+  GemmArgs f{};
+  f.A = bws.xm;
+  f.lda = kHidden;
+  f.B = B(w->final_linear);
+  f.ldb = kHidden;
+  f.M = 2 * r.n_img;
+  f.N = 128;
+  f.K = kHidden;
+  f.epi = GemmEpi::kStoreF32;
+  f.C = s.v_pair;
+  f.ldc = 128;
+  launch_gemm(f, stream);
+  launch_cfg_combine(s.v_pair, s.v_pair + (size_t)r.n_img * 128, v, r.n_img * 128, guidance, stream);
+  return check_launch("stack_forward_cfg");
+}
+
+size_t sample_cfg_ws_bytes(const CfgRows& r) {
+  return cfg_ws_bytes(r) + align256((size_t)r.n_img * 128 * 4) + align256((size_t)r.n_img * 128 * 2);
+}
+
+bool cfg_rows_ok(int n_img, int n_cond, int n_t0, int n_t1) {
+  return n_img > 0 && n_cond >= 0 && n_t0 >= 0 && n_t1 >= 0 &&
+         (long)n_img * 2 + (long)n_cond * 2 + n_t0 + n_t1 < (1L << 30);
+}
+}  // namespace
+
+extern "C" {
+
+int flux3_build_ids_cfg(int img_h, int img_w, int n_refs, const int* ref_hw, int n_txt0, int n_txt1,
+                        float* ids, int* n_out) {
+  REQUIRE(n_txt0 >= 0 && n_txt1 >= 0, FLUX3_EINVAL, "text lengths must be non-negative");
+  REQUIRE(n_out != nullptr, FLUX3_EINVAL, "n_out is null");
+  int n0 = 0, nshared = 0;
+  int rc = flux3_build_ids(img_h, img_w, n_refs, ref_hw, n_txt0, nullptr, &n0);
+  if (rc) return rc;
+  rc = flux3_build_ids(img_h, img_w, n_refs, ref_hw, 0, nullptr, &nshared);
+  if (rc) return rc;
+  const long n = (long)n0 + n_txt1 + nshared;
+  REQUIRE(n < (1L << 30), FLUX3_EINVAL, "too many tokens");
+  *n_out = (int)n;
+  if (!ids) return FLUX3_OK;
+  // sample 0: image | references | text 0 (text index 0 ..)
+  rc = flux3_build_ids(img_h, img_w, n_refs, ref_hw, n_txt0, ids, &n0);
+  if (rc) return rc;
+  float* p = ids + (size_t)n0 * 4;
+  // sample 1: text 1 | image | references
+  for (int i = 0; i < n_txt1; ++i) {
+    p[0] = 0.f; p[1] = 0.f; p[2] = 0.f; p[3] = (float)i;
+    p += 4;
+  }
+  return flux3_build_ids(img_h, img_w, n_refs, ref_hw, 0, p, &nshared);
+}
+
+size_t flux3_stack_cfg_workspace_size(int n_img, int n_cond, int n_txt0, int n_txt1) {
+  if (!cfg_rows_ok(n_img, n_cond, n_txt0, n_txt1)) return 0;
+  return cfg_ws_bytes(CfgRows{n_img, n_cond, n_txt0, n_txt1});
+}
+
+int flux3_stack_forward_cfg(const flux3_model_weights* w, const uint16_t* img, int n_img,
+                            const uint16_t* cond, int n_cond, const uint16_t* txt0, int n_txt0,
+                            const uint16_t* txt1, int n_txt1, const float* table, float sigma,
+                            float sigma_next, float guidance, float* v, void* workspace,
+                            size_t ws_bytes, hipStream_t stream) {
+  const CfgRows r{n_img, n_cond, n_txt0, n_txt1};
+  REQUIRE(std::isfinite(guidance), FLUX3_EINVAL, "guidance is not finite");
+  int rc = check_cfg_args(w, img, r, cond, txt0, txt1, table, v, workspace);
+  if (rc) return rc;
+  REQUIRE(ws_bytes >= cfg_ws_bytes(r), FLUX3_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes,
+          cfg_ws_bytes(r));
+  return stack_cfg_unchecked(w, img, cond, txt0, txt1, r, table, sigma, sigma_next, guidance, v,
+                             workspace, stream);
+}
+
+size_t flux3_sample_cfg_workspace_size(int n_img, int n_cond, int n_txt0, int n_txt1) {
+  if (!cfg_rows_ok(n_img, n_cond, n_txt0, n_txt1)) return 0;
+  return sample_cfg_ws_bytes(CfgRows{n_img, n_cond, n_txt0, n_txt1});
+}
+
+int flux3_sample_cfg(const flux3_model_weights* w, float* x, int n_img, const uint16_t* cond,
+                     int n_cond, const uint16_t* txt0, int n_txt0, const uint16_t* txt1, int n_txt1,
+                     const float* table, const float* sigmas, int steps, float guidance,
+                     void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const CfgRows r{n_img, n_cond, n_txt0, n_txt1};
+  REQUIRE(steps >= 0, FLUX3_EINVAL, "steps=%d", steps);
+  REQUIRE(steps == 0 || sigmas != nullptr, FLUX3_EINVAL, "sigmas is null");
+  for (int k = 0; k <= steps && steps > 0; ++k)
+    REQUIRE(std::isfinite(sigmas[k]), FLUX3_EINVAL, "sigmas[%d] is not finite", k);
+  REQUIRE(std::isfinite(guidance), FLUX3_EINVAL, "guidance is not finite");
+  REQUIRE_PTR(x);
+  // x doubles as the latent and velocity pointers for the shared checks.
+  int rc = check_cfg_args(w, (const uint16_t*)x, r, cond, txt0, txt1, table, x, workspace);
+  if (rc) return rc;
+  REQUIRE(ws_bytes >= sample_cfg_ws_bytes(r), FLUX3_EWORKSPACE, "workspace %zu < %zu bytes",
+          ws_bytes, sample_cfg_ws_bytes(r));
+  if (steps == 0) return FLUX3_OK;
+  char* p = (char*)workspace + cfg_ws_bytes(r);
+  float* v = (float*)p;
+  bf16* xb = (bf16*)(p + align256((size_t)n_img * 128 * 4));
+  const int n_lat = n_img * 128;
+  launch_euler(x, xb, nullptr, n_lat, 0.f, stream);  // xb = bf16(x)
+  for (int k = 0; k < steps; ++k) {
+    rc = stack_cfg_unchecked(w, (const uint16_t*)xb, cond, txt0, txt1, r, table, sigmas[k],
+                             sigmas[k + 1], guidance, v, workspace, stream);
+    if (rc) return rc;
+    launch_euler(x, k + 1 < steps ? xb : nullptr, v, n_lat, sigmas[k + 1] - sigmas[k], stream);
+  }
+  return check_launch("sample_cfg");
 }
 
 }  // extern "C"

@@ -102,6 +102,20 @@ void launch_euler(float* x, bf16* xb, const float* v, int n, float dt, hipStream
   hipLaunchKernelGGL(euler_kernel, dim3((n + 255) / 256), dim3(256), 0, st, x, xb, v, n, dt);
 }
 
+// Classifier-free guidance: v = vu + g (vc - vu).
+__global__ void cfg_combine_kernel(const float* __restrict__ vu, const float* __restrict__ vc,
+                                   float* __restrict__ v, int n, float g) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float a = vu[i];
+  v[i] = a + g * (vc[i] - a);
+}
+
+void launch_cfg_combine(const float* vu, const float* vc, float* v, int n, float g, hipStream_t st) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(cfg_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, st, vu, vc, v, n, g);
+}
+
 // Weight packing (one-time).  w_in rows: q | k | v, then mlp_in with the a/b
 // halves interleaved in groups of 32 rows.  w_out: [attn_out | mlp_out].
 // One 16-byte chunk per thread.

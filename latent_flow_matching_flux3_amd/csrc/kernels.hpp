@@ -68,6 +68,7 @@ struct Timesteps {
 void launch_timestep_embedding(const Timesteps& ts, int nt, float* out, hipStream_t st);
 void launch_gemv(const GemvBatch& batch, int nb, int rows, int K, bool silu_x, bool accumulate,
                  hipStream_t st);
+void launch_cfg_combine(const float* vu, const float* vc, float* v, int n, float g, hipStream_t st);
 void launch_euler(float* x, bf16* xb, const float* v, int n, float dt, hipStream_t st);
 void launch_pack_block(const bf16* wq, const bf16* wk, const bf16* wv, const bf16* wo,
                        const bf16* w_mlp_in, const bf16* w_mlp_out, bf16* w_in, bf16* w_out,

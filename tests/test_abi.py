@@ -46,6 +46,18 @@ def test_build_ids_matches_oracle(L):
         np.testing.assert_array_equal(ids, O.build_ids(h, w, nt, refs))
 
 
+def test_build_ids_cfg_is_the_two_samples_ids(L):
+    """Packed ids = sample 0's ids (image, refs, text 0), then sample 1's
+    text ids and its image and reference ids (bit-exact)."""
+    for h, w, n0, n1, refs in [(2, 3, 2, 3, [(1, 2)]), (4, 4, 80, 512, []), (3, 5, 0, 7, [(2, 2), (1, 3)])]:
+        got = L.flux3_build_ids_cfg(h, w, n0, n1, refs).numpy().astype(np.float64)
+        s0 = O.build_ids(h, w, n0, refs)
+        s1 = O.build_ids(h, w, n1, refs)
+        n_shared = h * w + sum(a * b for a, b in refs)
+        want = np.concatenate([s0, s1[n_shared:], s1[:n_shared]])
+        np.testing.assert_array_equal(got, want)
+
+
 def test_sigmas_match_oracle(L):
     for steps in (1, 16, 50):
         np.testing.assert_allclose(L.flux3_sigmas(steps).numpy(), O.sigmas(steps), rtol=1e-7, atol=1e-7)

@@ -24,9 +24,11 @@ def L():
 class Weights:
     """Seeded weights: device copies for the library, float64 views for the oracle."""
 
-    def __init__(self, L, seed, lay, n_early, n_single):
+    def __init__(self, L, seed, lay, n_early, n_single, base=False):
+        """base: the base checkpoint's tensor set (no ref_time_in)."""
         self.seed = seed
-        self.glob_cpu = {k: syn.global_weight(seed, k) for k in syn.GLOBAL_SHAPES}
+        self.glob_cpu = {k: syn.global_weight(seed, k) for k in syn.GLOBAL_SHAPES
+                         if not (base and k.startswith("ref_time_in."))}
         glob = {k: dev(v) for k, v in self.glob_cpu.items()}
         modes = ["image"] + (["image_cond"] if lay.n_cond else []) + ["txt"]
         early = {}
@@ -216,3 +218,83 @@ def test_sample_graph_replays(L):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(xg, xe), f"replay {r} differs from the eager call"
+
+
+def _cfg_case(L, seed, lay, n_txt1, n_early=1, n_single=1):
+    wts = Weights(L, seed, lay, n_early, n_single, base=True)
+    img, cond, txt0 = _inputs(lay, seed)          # txt0: the empty prompt (lay.n_txt rows)
+    txt1 = syn.text_features(seed + 4, n_txt1)    # the prompt
+    ids = L.flux3_build_ids_cfg(lay.img_h, lay.img_w, lay.n_txt, n_txt1, lay.refs).to("cuda")
+    table = L.flux3_rope_table(ids)
+    return wts, img, cond, txt0, txt1, table
+
+
+def _oracle_velocity(wts, lay, cond, txts, n_early, n_single):
+    def velocity(x, sigma, i):
+        return O.stack_forward(wts.W, wts.B, x, None if cond is None else f64(cond), f64(txts[i]),
+                               lay.img_h, lay.img_w, lay.refs, sigma, None, n_early, n_single)
+    return velocity
+
+
+def test_stack_cfg_pack(L):
+    """The base checkpoint's guided pack (image and references shared through
+    stage 1, texts side by side, both samples in one stage-2 pass) against
+    the oracle's two separate stacks and guidance; also against two separate
+    GPU stack calls."""
+    lay = syn.Layout(3, 5, 80, [(2, 3), (3, 2)])
+    n_txt1 = 160
+    seed = 330
+    g = 3.5
+    wts, img, cond, txt0, txt1, table = _cfg_case(L, seed, lay, n_txt1)
+    say(f"stack cfg pack n_img={lay.n_img} n_cond={lay.n_cond} texts {lay.n_txt}/{n_txt1}")
+    ws = L.workspace(L.flux3_stack_cfg_workspace_size(lay.n_img, lay.n_cond, lay.n_txt, n_txt1))
+    v = torch.empty((lay.n_img, 128), dtype=torch.float32, device="cuda")
+    sig = 0.8739
+    L.flux3_stack_forward_cfg(wts.model, dev(img), dev(cond), dev(txt0), dev(txt1), table, sig, 0.0, g, v, ws)
+    torch.cuda.synchronize()
+    vel = _oracle_velocity(wts, lay, cond, [txt0, txt1], 1, 1)
+    v0, v1 = vel(f64(img), sig, 0), vel(f64(img), sig, 1)
+    assert_agree(f64(v), O.cfg_velocity(v0, v1, g), "cfg pack vs oracle")
+    # the same two samples through flux3_stack_forward one at a time
+    outs = []
+    for t in (txt0, txt1):
+        ids = L.flux3_build_ids(lay.img_h, lay.img_w, t.shape[0], lay.refs).to("cuda")
+        sws = L.workspace(L.flux3_stack_workspace_size(lay.n_img, lay.n_cond, t.shape[0]))
+        vi = torch.empty((lay.n_img, 128), dtype=torch.float32, device="cuda")
+        L.flux3_stack_forward(wts.model, dev(img), dev(cond), dev(t), L.flux3_rope_table(ids), sig, 0.0, vi, sws)
+        outs.append(f64(vi))
+    torch.cuda.synchronize()
+    # (rounding differs only through accumulation order, e.g. split-K choices
+    # that depend on the row count; guidance amplifies it 3.5 times)
+    assert_agree(f64(v), outs[0] + g * (outs[1] - outs[0]), "cfg pack vs two separate calls")
+    # guidance 1: the prompt's velocity alone
+    L.flux3_stack_forward_cfg(wts.model, dev(img), dev(cond), dev(txt0), dev(txt1), table, sig, 0.0, 1.0, v, ws)
+    torch.cuda.synchronize()
+    assert_agree(f64(v), v1, "cfg pack guidance 1 vs oracle prompt velocity")
+
+
+def test_sample_cfg(L):
+    """The guided sampler in one call: bit-identical to step-by-step guided
+    stack calls + Euler updates, and within tolerance of the oracle's
+    base-checkpoint sampler (3 steps of the shifted schedule)."""
+    lay = syn.Layout(4, 4, 80)
+    n_txt1 = 240
+    seed = 340
+    steps, g = 3, 3.5
+    wts, img, cond, txt0, txt1, table = _cfg_case(L, seed, lay, n_txt1)
+    sig = L.flux3_sigmas(steps)
+    say(f"sample cfg n_img={lay.n_img} texts {lay.n_txt}/{n_txt1} steps={steps}")
+    ws = L.workspace(L.flux3_sample_cfg_workspace_size(lay.n_img, 0, lay.n_txt, n_txt1))
+    x = dev(img).float()
+    L.flux3_sample_cfg(wts.model, x, None, dev(txt0), dev(txt1), table, sig, g, ws)
+    xs, xb = dev(img).float(), dev(img)
+    v = torch.empty((lay.n_img, 128), dtype=torch.float32, device="cuda")
+    cws = L.workspace(L.flux3_stack_cfg_workspace_size(lay.n_img, 0, lay.n_txt, n_txt1))
+    sl = sig.tolist()
+    for k in range(steps):
+        L.flux3_stack_forward_cfg(wts.model, xb, None, dev(txt0), dev(txt1), table, sl[k], sl[k + 1], g, v, cws)
+        L.flux3_euler_step(xs, xb, v, sl[k], sl[k + 1])
+    torch.cuda.synchronize()
+    assert torch.equal(x, xs), "flux3_sample_cfg differs from the step-by-step loop"
+    xr = O.sample_base_cfg(_oracle_velocity(wts, lay, None, [txt0, txt1], 1, 1), f64(img), steps, g)
+    assert_agree(f64(x), xr, f"cfg sampler {steps} steps")
