@@ -38,6 +38,11 @@ function that uses it):
   R12 all references of a sample form one image_cond stream in stage 1.
   R14 attn_out is applied to the attention output (a listed tensor), though
       the blog's block sketch folds it away.
+  R17 fp8r ("rowwise FP8"): each row of a projection's input (per token) and
+      of its weight (per output row) gets scale = row max / 448 and is
+      rounded to OCP E4M3; products accumulate exactly and are scaled after
+      the dot product.  The output projection is one product over [o | swiglu]
+      against [attn_out | mlp_out], so those row scales span both parts.
 """
 from __future__ import annotations
 
@@ -229,6 +234,96 @@ def block_forward(x: np.ndarray, segments, mods: np.ndarray, w: dict, ids: np.nd
     a, b = ab[:, :MLP_HIDDEN], ab[:, MLP_HIDDEN:]
     mlp = (silu(a) * b) @ w["mlp_out"].T
     return x[rows] + gate[rows] * (att + mlp)
+
+
+# ----------------------------------------------------------------------------
+# fp8r: rowwise FP8 projections ([blog] §Base model and quantized variants:
+# the transformer also ships as "fp8r (rowwise FP8)"), in the OCP E4M3 format
+# of CDNA4's FP8 units (R17)
+# ----------------------------------------------------------------------------
+
+E4M3_MAX = 448.0   # largest finite E4M3 value: 1.75 * 2^8
+
+
+def e4m3_round(x):
+    """Nearest OCP E4M3 value of float32 input: 1 sign bit, 4 exponent bits
+    (bias 7), 3 mantissa bits; normals 2^-6 .. 448, subnormals k * 2^-9; no
+    infinities.  Ties go to the even mantissa; magnitudes past 448 saturate.
+    Returns (codes uint8, values float64)."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(np.maximum(a, 2.0 ** -6))      # a = m 2^ex, m in [0.5, 1)
+    e = np.minimum(ex - 1, 8)                        # binade 2^e (subnormals: e = -6)
+    q = np.ldexp(1.0, e - 3)                         # value spacing in that binade
+    v = np.minimum(np.rint(a / q) * q, E4M3_MAX)     # rint: ties to even
+    # encode: normals E = e' + 7, M = v / 2^(e'-3) - 8; subnormals E = 0, M = v / 2^-9
+    _, ev = np.frexp(np.where(v > 0, v, 1.0))
+    ev = ev - 1
+    normal = v >= 2.0 ** -6
+    big_e = np.where(normal, ev + 7, 0)
+    man = np.where(normal, v / np.ldexp(1.0, ev - 3) - 8, v / 2.0 ** -9)
+    codes = (np.signbit(x).astype(np.uint16) << 7) | (big_e.astype(np.uint16) << 3) | man.astype(np.uint16)
+    return codes.astype(np.uint8), np.where(np.signbit(x), -v, v)
+
+
+def e4m3_value(codes):
+    """Value of E4M3 codes (inverse of the encoding above; 0x7F/0xFF are NaN)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    big_e, man = (c >> 3) & 15, c & 7
+    mag = np.where(big_e > 0, np.ldexp(1.0 + man / 8.0, big_e - 7), man * 2.0 ** -9)
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def quantize_rows_fp8(x):
+    """Rowwise FP8 (R17): per row, scale = max|x| / 448 and codes of
+    x * (448 / max|x|), the scale, its reciprocal and the product each taken
+    in float32 (the precision in which the codes are decided); a row of zeros
+    gets scale 1.  Returns (codes uint8, scale float32 per row, dequantized
+    float64 = value * scale)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=1)
+    nz = amax > 0
+    safe = np.where(nz, amax, np.float32(1))
+    inv = np.where(nz, np.float32(E4M3_MAX) / safe, np.float32(1)).astype(np.float32)
+    scale = np.where(nz, safe / np.float32(E4M3_MAX), np.float32(1)).astype(np.float32)
+    codes, vals = e4m3_round((x32 * inv[:, None]).astype(np.float32))
+    return codes, scale, vals * scale.astype(np.float64)[:, None]
+
+
+def fp8r_linear(a: np.ndarray, w: np.ndarray, quant=quantize_rows_fp8) -> np.ndarray:
+    """a w^T with both operands quantized per row (a per token, w per output
+    row), the dot products exact and scaled afterwards (R17)."""
+    return quant(a)[2] @ quant(w)[2].T
+
+
+def block_forward_fp8r(x: np.ndarray, segments, mods: np.ndarray, w: dict, ids: np.ndarray,
+                       rows=None, quant=quantize_rows_fp8) -> np.ndarray:
+    """block_forward with its two large projections as rowwise-FP8 products
+    (R17): h through [q | k | v | mlp_in] (one activation scale per token, one
+    weight scale per output row of each matrix), and [o | swiglu] through
+    [attn_out | mlp_out] as one product over the 12288 concatenated inputs
+    (one scale per token row and per output row across both).  Everything
+    else as in block_forward."""
+    n = x.shape[0]
+    shift, scale, gate = rows_modulation(n, segments, mods)
+    h = modulate(layer_norm(x), shift, scale)
+    if rows is None:
+        rows = np.arange(n)
+    w_in = np.concatenate([w["q_proj"], w["k_proj"], w["v_proj"], w["mlp_in"]], axis=0)
+    proj = fp8r_linear(h, w_in, quant)                # [n, 3*3072 + 2*9216]
+    q = proj[rows, :HIDDEN].reshape(-1, HEADS, HEAD_DIM)
+    k = proj[:, HIDDEN:2 * HIDDEN].reshape(n, HEADS, HEAD_DIM)
+    v = proj[:, 2 * HIDDEN:3 * HIDDEN].reshape(n, HEADS, HEAD_DIM)
+    q = apply_rope(rms_norm(q, w["norm.query_norm.scale"]), ids[rows])
+    k = apply_rope(rms_norm(k, w["norm.key_norm.scale"]), ids)
+    o = attention(q, k, v).reshape(-1, HIDDEN)
+    ab = proj[rows, 3 * HIDDEN:]
+    a, b = ab[:, :MLP_HIDDEN], ab[:, MLP_HIDDEN:]
+    cat = np.concatenate([o, silu(a) * b], axis=1)
+    w_out = np.concatenate([w["attn_out"], w["mlp_out"]], axis=1)
+    return x[rows] + gate[rows] * fp8r_linear(cat, w_out, quant)
 
 
 # ----------------------------------------------------------------------------

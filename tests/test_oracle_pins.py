@@ -529,3 +529,82 @@ def test_longest_sequence():
     l_axis = ids[lay.n_img:lay.n_img + lay.n_cond, 3]
     assert sorted(set(l_axis.tolist())) == [-float(k) for k in range(10, 0, -1)]
     assert (ids[lay.n_img + lay.n_cond:, 3] == range(lay.n_txt)).all()
+
+
+# ---- fp8r (rowwise FP8, R17) --------------------------------------------------
+
+def test_e4m3_rounding_against_torch():
+    """OCP E4M3 rounding (ties to even) agrees code for code with torch's
+    float8_e4m3fn conversion over the finite range, including exact ties
+    and subnormals."""
+    rng = np.random.default_rng(0)
+    mag = np.exp2(rng.uniform(-12, np.log2(448.0), 200000))
+    x = (mag * rng.choice([-1.0, 1.0], mag.size)).astype(np.float32)
+    grid = O.e4m3_value(np.arange(0, 0x7F))                 # every finite non-negative value
+    ties = ((grid[1:] + grid[:-1]) / 2).astype(np.float32)  # midpoints (exact in float32)
+    x = np.concatenate([x, ties, -ties, grid.astype(np.float32), np.float32([448.0, -448.0, 0.0])])
+    codes, vals = O.e4m3_round(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn)
+    np.testing.assert_array_equal(codes, ref.view(torch.uint8).numpy())
+    np.testing.assert_array_equal(vals, ref.to(torch.float64).numpy())
+
+
+def test_e4m3_closed_forms():
+    cases = {448.0: 0x7E, 2.0 ** -9: 0x01, -1.0: 0xB8, 1.0: 0x38, 1.0625: 0x38, 1.1875: 0x3A,
+             3 * 2.0 ** -10: 0x02, 2.0 ** -10: 0x00, 240.0: 0x77, 2.0 ** -6: 0x08, 0.875 * 2.0 ** -6: 0x07}
+    codes, _ = O.e4m3_round(np.array(list(cases), np.float32))
+    assert [int(c) for c in codes] == list(cases.values())
+    # every finite code decodes and re-encodes to itself; 0x7F is NaN
+    all_codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    back, _ = O.e4m3_round(O.e4m3_value(all_codes).astype(np.float32))
+    assert np.array_equal(back[all_codes != 0x80], all_codes[all_codes != 0x80])
+    assert np.isnan(O.e4m3_value([0x7F, 0xFF])).all()
+    assert O.e4m3_round(np.float32([1e6, -1e6]))[1].tolist() == [448.0, -448.0]   # saturates
+
+
+def test_rowwise_fp8_quantization_properties():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((64, 300)) * np.exp2(rng.integers(-8, 8, (64, 1)))).astype(np.float32)
+    x[5] = 0.0
+    codes, scale, deq = O.quantize_rows_fp8(x)
+    amax = np.abs(x).max(axis=1)
+    hit = np.abs(x) == amax[:, None]
+    assert set(codes[hit & (amax[:, None] > 0)].tolist()) <= {0x7E, 0xFE}   # the row max lands on 448
+    assert (codes[5] == 0).all() and scale[5] == 1.0 and (deq[5] == 0).all()
+    # half a spacing: 2^-4 relative for normals, 2^-10 * scale below 2^-6 * scale
+    err = np.abs(deq - x.astype(np.float64))
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale[:, None].astype(np.float64))
+    assert (err <= bound * (1 + 1e-9)).all()
+
+
+def test_fp8r_linear_exact_on_representable_rows():
+    """Rows made of E4M3 values times a power of two, with the row max at
+    448 times that power, quantize exactly: the FP8 product equals the exact
+    product (catches a misplaced or transposed scale)."""
+    rng = np.random.default_rng(2)
+    grid = O.e4m3_value(np.arange(1, 0x7F))
+    def rows(n, k):
+        v = rng.choice(grid, (n, k)) * rng.choice([-1.0, 1.0], (n, k))
+        v[:, 0] = 448.0
+        return v * np.exp2(rng.integers(-20, 5, (n, 1)))
+    a, w = rows(9, 64), rows(13, 64)
+    np.testing.assert_allclose(O.fp8r_linear(a, w), a @ w.T, rtol=1e-13)
+
+
+def test_fp8r_block_structure_matches_block_forward():
+    """With the quantizer replaced by the identity, the fp8r block (one fused
+    input projection, one output projection over [o | swiglu]) is the plain
+    block, which is pinned to torch's layers; with FP8 it stays close."""
+    rng = np.random.default_rng(3)
+    n = 12
+    w = {k: f64(v) for k, v in syn.block_weights(5, "single_blocks.0").items()}
+    x = rng.standard_normal((n, O.HIDDEN))
+    mods = rng.standard_normal((1, 3, O.HIDDEN)) * 0.3
+    ids = O.build_ids(2, 3, 6)
+    ident = lambda a: (None, None, np.asarray(a, np.float64))
+    ref = O.block_forward(x, [(0, n)], mods, w, ids)
+    np.testing.assert_allclose(O.block_forward_fp8r(x, [(0, n)], mods, w, ids, quant=ident), ref,
+                               rtol=1e-10, atol=1e-10)
+    got = O.block_forward_fp8r(x, [(0, n)], mods, w, ids)
+    d, r = got - x, ref - x
+    assert float((d * r).sum() / np.linalg.norm(d) / np.linalg.norm(r)) > 0.99
