@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the fp8r (rowwise FP8 projections) stack step")
     ap.add_argument("--no-cfg", action="store_true",
                     help="skip the base checkpoint's guided 50-step sampling")
     ap.add_argument("--no-long", action="store_true",
@@ -192,6 +194,31 @@ def sampler_loop(L, torch, model, img, txt, table, n_img: int, n_txt: int, steps
     return {"tokens": n, "steps": steps, "eager_ms_per_image": round(eager, 3),
             "graph_ms_per_image": round(graph_ms, 3), "graph_steps_per_s": round(steps * 1e3 / graph_ms, 2),
             "graph_tflops": round(steps * stack_flops(n_img, 0, n_txt) / (graph_ms * 1e-3) / 1e12, 1)}
+
+
+def fp8r(L, torch, syn, model, img, txt, table, n_img: int, n_txt: int, seed: int):
+    """The same transformer with fp8r blocks (rowwise E4M3 projections, from
+    the same weights): one stack step at 4608 tokens (3 timed after a
+    warm-up), and one joint block at 4608 rows in bf16 and fp8 (5 each)."""
+    q = L.ModelWeights(model.glob, {m: [b.fp8_copy() for b in bl] for m, bl in model.early.items()},
+                       [b.fp8_copy() for b in model.single])
+    ws = L.workspace(L.flux3_stack_workspace_size(n_img, 0, n_txt))
+    v = torch.empty((n_img, 128), dtype=torch.float32, device="cuda")
+    sig = L.flux3_sigmas(16).tolist()
+    ms = event_time_ms(torch, lambda: L.flux3_stack_forward(q, img, None, txt, table, sig[0], sig[1], v, ws), 3)
+    assert torch.isfinite(v).all().item(), "non-finite velocity"
+    n = n_img + n_txt
+    x = torch.randn((n, HIDDEN), device="cuda", generator=torch.Generator(device="cuda").manual_seed(seed))
+    mod = torch.randn((2, 3, HIDDEN), device="cuda", generator=torch.Generator(device="cuda").manual_seed(seed + 1)) * 0.1
+    bws = L.workspace(L.flux3_block_workspace_size(n))
+    segs = [0, n_img, n]
+    blk = {"bf16": model.single[0], "fp8": q.single[0]}
+    block_ms = {k: round(event_time_ms(torch, lambda b=b: L.flux3_block_forward(x, segs, mod, b, table, bws), 5), 4)
+                for k, b in blk.items()}
+    f = stack_flops(n_img, 0, n_txt)
+    del q, ws, bws
+    return {"workload": "stack_t2i_1024_4608tok", "ms_per_step": round(ms, 3), "tflops": round(f / (ms * 1e-3) / 1e12, 1),
+            "joint_block_ms": block_ms, "mfma_dtype": "fp8 e4m3 (block projections), bf16 elsewhere"}
 
 
 def cfg_flops(n_img: int, n_t0: int, n_t1: int, n_early: int = 5, n_single: int = 28) -> float:
@@ -409,6 +436,11 @@ def main():
         s_table = L.flux3_rope_table(L.flux3_build_ids(small.img_h, small.img_w, small.n_txt).to("cuda"))
         loops["96tok"] = sampler_loop(L, torch, model, s_img, s_txt, s_table, small.n_img, small.n_txt, 16)
 
+    fp8 = None
+    if not args.no_fp8:
+        print("[bench] fp8r blocks: stack step and one joint block", file=sys.stderr, flush=True)
+        fp8 = fp8r(L, torch, syn, model, img, txt, table, n_img, n_txt, args.seed + 11)
+
     cfg = None
     if not args.no_cfg:
         print("[bench] base checkpoint: guided pack, 50-step loop", file=sys.stderr, flush=True)
@@ -447,6 +479,7 @@ def main():
         "roofline": roof,
         "kernels": per_kernel,
         "sampler_loop": loops,
+        "fp8r": fp8,
         "cfg_base": cfg,
         "long_context": long_ctx,
         "cpu_baseline": cpu,

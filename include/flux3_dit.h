@@ -160,10 +160,17 @@ int flux3_linear(const uint16_t* x, int ldx, const uint16_t* w, int ldw, uint16_
  *         dimension, so attn_out(o) + mlp_out(h) is one product with [o | h].
  */
 typedef struct flux3_block_weights {
-  const uint16_t* w_in;     /* device [27648][3072] bf16 */
-  const uint16_t* w_out;    /* device [3072][12288] bf16 */
+  const uint16_t* w_in;     /* device [27648][3072] bf16 (NULL when w_in_fp8 is set) */
+  const uint16_t* w_out;    /* device [3072][12288] bf16 (NULL when w_out_fp8 is set) */
   const uint16_t* q_scale;  /* device [128] bf16 */
   const uint16_t* k_scale;  /* device [128] bf16 */
+  /* fp8r ([blog] "Base model and quantized variants": rowwise FP8): when set
+   * (from flux3_pack_block_fp8), the block's two projections run as rowwise
+   * E4M3 products, their inputs quantized per token on the fly. */
+  const uint8_t* w_in_fp8;  /* device [27648][3072] OCP E4M3 codes */
+  const float* w_in_scale;  /* device [27648] fp32 */
+  const uint8_t* w_out_fp8; /* device [3072][12288] */
+  const float* w_out_scale; /* device [3072] */
 } flux3_block_weights;
 
 #define FLUX3_W_IN_ROWS 27648
@@ -175,6 +182,34 @@ typedef struct flux3_block_weights {
 int flux3_pack_block(const uint16_t* q_proj, const uint16_t* k_proj, const uint16_t* v_proj,
                      const uint16_t* attn_out, const uint16_t* mlp_in, const uint16_t* mlp_out,
                      uint16_t* w_in, uint16_t* w_out, hipStream_t stream);
+
+/* ---- fp8r: rowwise FP8 ([blog] "Base model and quantized variants") --------------
+ * A row's scale is max|row| / 448 and its codes are OCP E4M3 (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits, largest 448) of
+ * row * (448 / max|row|), rounded to nearest even; scale, inverse and product
+ * in fp32; a row of zeros gets scale 1.  A product of two such operands is
+ * (codes_a codes_w^T) scaled by scale_a[row] * scale_w[col], accumulated in
+ * fp32.
+ *
+ * flux3_quantize_rows_fp8: rows x [rows][cols] bf16 (ldx elements, cols a
+ *   multiple of 8, 16-byte aligned rows) -> q [rows][ldq] codes (ldq a
+ *   multiple of 8, q 8-byte aligned), scale [rows]. */
+int flux3_quantize_rows_fp8(const uint16_t* x, int ldx, int rows, int cols, uint8_t* q, int ldq,
+                            float* scale, hipStream_t stream);
+
+/* flux3_pack_block_fp8: quantize a packed block's w_in and w_out (from
+ * flux3_pack_block) per row into the fp8 fields' buffers (caller-allocated,
+ * sizes as in flux3_block_weights). */
+int flux3_pack_block_fp8(const uint16_t* w_in, const uint16_t* w_out, uint8_t* w_in_fp8,
+                         float* w_in_scale, uint8_t* w_out_fp8, float* w_out_scale, hipStream_t stream);
+
+/* flux3_linear_fp8: y = (a w^T) * a_scale[row] * w_scale[col] for quantized
+ * a [m][k] (lda bytes) and w [n][k] (ldw bytes), into y (bf16, ldy elements)
+ * or y_f32 (exactly one non-NULL).  Requires n % 256 == 0, k % 128 == 0,
+ * k >= 256, lda and ldw multiples of 16, 16-byte aligned pointers. */
+int flux3_linear_fp8(const uint8_t* a, int lda, const float* a_scale, const uint8_t* w, int ldw,
+                     const float* w_scale, uint16_t* y, float* y_f32, int ldy, int m, int n, int k,
+                     hipStream_t stream);
 
 /* ---- a4 + a5: the block's input projections, one fused product ------------------
  * [q | k | v] = xm [Wq; Wk; Wv]^T and h = silu(a) * b with [a | b] = xm mlp_in^T

@@ -41,7 +41,8 @@ S = C.c_size_t
 
 
 class BlockWeightsC(C.Structure):
-    _fields_ = [("w_in", P), ("w_out", P), ("q_scale", P), ("k_scale", P)]
+    _fields_ = [("w_in", P), ("w_out", P), ("q_scale", P), ("k_scale", P),
+                ("w_in_fp8", P), ("w_in_scale", P), ("w_out_fp8", P), ("w_out_scale", P)]
 
 
 class ModelWeightsC(C.Structure):
@@ -80,6 +81,9 @@ _SIGS = {
     "flux3_stack_forward_cfg": (I, [C.POINTER(ModelWeightsC), P, I, P, I, P, I, P, I, P, F, F, F, P, P, S, P]),
     "flux3_sample_cfg_workspace_size": (S, [I, I, I, I]),
     "flux3_sample_cfg": (I, [C.POINTER(ModelWeightsC), P, I, P, I, P, I, P, I, P, P, I, F, P, S, P]),
+    "flux3_quantize_rows_fp8": (I, [P, I, I, I, P, I, P, P]),
+    "flux3_pack_block_fp8": (I, [P, P, P, P, P, P, P]),
+    "flux3_linear_fp8": (I, [P, I, P, P, I, P, P, P, I, I, I, I, P]),
     "flux3_euler_step": (I, [P, P, P, I, F, F, P]),
     "flux3_sigmas": (I, [I, C.c_double, P]),
 }
@@ -214,16 +218,68 @@ def flux3_pack_block(w: dict, device=None, stream=None):
     return w_in, w_out
 
 
-class PackedBlock:
-    """Device tensors of one packed block; keeps them alive for the C struct."""
+def flux3_quantize_rows_fp8(x, q=None, scale=None, stream=None):
+    """Rowwise FP8 of a device bf16 [rows, cols] tensor: (codes uint8 [rows, cols], scale fp32 [rows])."""
+    _require_dev(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
+    scale = torch.empty(rows, dtype=torch.float32, device=x.device) if scale is None else scale
+    _check(lib().flux3_quantize_rows_fp8(_ptr(x), _ld(x), rows, cols, _ptr(q), _ld(q), _ptr(scale),
+                                         _stream(stream)))
+    return q, scale
 
-    def __init__(self, w: dict, stream=None):
+
+def flux3_linear_fp8(a, a_scale, w, w_scale, y=None, y_f32=None, stream=None):
+    m, k = a.shape
+    n = w.shape[0]
+    _check(lib().flux3_linear_fp8(_ptr(a), _ld(a), _ptr(a_scale), _ptr(w), _ld(w), _ptr(w_scale), _ptr(y),
+                                  _ptr(y_f32), _ld(y) if y is not None else _ld(y_f32), m, n, k,
+                                  _stream(stream)))
+    return y if y is not None else y_f32
+
+
+class PackedBlock:
+    """Device tensors of one packed block; keeps them alive for the C struct.
+    fp8=True: the projections are quantized per row (fp8r) and the bf16
+    packed weights are dropped."""
+
+    def __init__(self, w: dict, stream=None, fp8: bool = False):
         self.w_in, self.w_out = flux3_pack_block(w, stream=stream)
         self.q_scale = w["norm.query_norm.scale"].contiguous()
         self.k_scale = w["norm.key_norm.scale"].contiguous()
+        self.fp8 = None
+        if fp8:
+            dev = self.w_in.device
+            w_in8 = torch.empty((W_IN_ROWS, HIDDEN), dtype=torch.uint8, device=dev)
+            w_out8 = torch.empty((HIDDEN, W_OUT_COLS), dtype=torch.uint8, device=dev)
+            s_in = torch.empty(W_IN_ROWS, dtype=torch.float32, device=dev)
+            s_out = torch.empty(HIDDEN, dtype=torch.float32, device=dev)
+            _check(lib().flux3_pack_block_fp8(_ptr(self.w_in), _ptr(self.w_out), _ptr(w_in8), _ptr(s_in),
+                                              _ptr(w_out8), _ptr(s_out), _stream(stream)))
+            self.fp8 = (w_in8, s_in, w_out8, s_out)
+            torch.cuda.synchronize()  # the bf16 packed weights are read until here
+            self.w_in = self.w_out = None
+
+    def fp8_copy(self, stream=None) -> "PackedBlock":
+        """The same block with fp8r projections (new quantized buffers; this
+        block's bf16 weights are kept)."""
+        b = PackedBlock.__new__(PackedBlock)
+        b.q_scale, b.k_scale = self.q_scale, self.k_scale
+        dev = self.w_in.device
+        w_in8 = torch.empty((W_IN_ROWS, HIDDEN), dtype=torch.uint8, device=dev)
+        w_out8 = torch.empty((HIDDEN, W_OUT_COLS), dtype=torch.uint8, device=dev)
+        s_in = torch.empty(W_IN_ROWS, dtype=torch.float32, device=dev)
+        s_out = torch.empty(HIDDEN, dtype=torch.float32, device=dev)
+        _check(lib().flux3_pack_block_fp8(_ptr(self.w_in), _ptr(self.w_out), _ptr(w_in8), _ptr(s_in),
+                                          _ptr(w_out8), _ptr(s_out), _stream(stream)))
+        b.fp8 = (w_in8, s_in, w_out8, s_out)
+        b.w_in = b.w_out = None
+        return b
 
     def c(self) -> BlockWeightsC:
-        return BlockWeightsC(_ptr(self.w_in), _ptr(self.w_out), _ptr(self.q_scale), _ptr(self.k_scale))
+        f = self.fp8 or (None, None, None, None)
+        return BlockWeightsC(_ptr(self.w_in), _ptr(self.w_out), _ptr(self.q_scale), _ptr(self.k_scale),
+                             _ptr(f[0]), _ptr(f[1]), _ptr(f[2]), _ptr(f[3]))
 
 
 def flux3_block_in_proj(xm, w_in, qkv, h, stream=None):

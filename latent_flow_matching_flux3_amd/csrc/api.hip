@@ -60,14 +60,19 @@ bf16* B(uint16_t* p) { return reinterpret_cast<bf16*>(p); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Block workspace: xm [n][3072] | qkv [n][9216] | cat [n][12288], bf16.
-// The q|k|v region is dead once attention has run, so the output projection
-// borrows it as scratch for a K-split product (sized for that too).
+// Block workspace: xm [n][3072] | qkv [n][9216] | cat [n][12288], bf16, then
+// for fp8 blocks cat8 [n][12288] codes and the two row-scale vectors [n]
+// (the fp8 xm codes reuse the xm region).  The q|k|v region is dead once
+// attention has run, so the output projection borrows it as scratch for a
+// K-split product (sized for that too).
 struct BlockWs {
   bf16* xm;
   bf16* qkv;
   size_t qkv_bytes;
   bf16* cat;
+  uint8_t* cat8;
+  float* scale_in;
+  float* scale_out;
 };
 
 size_t qkv_region_bytes(int n) {
@@ -75,7 +80,8 @@ size_t qkv_region_bytes(int n) {
 }
 
 size_t block_ws_bytes(int n) {
-  return align256((size_t)n * kHidden * 2) + qkv_region_bytes(n) + align256((size_t)n * kWOutCols * 2);
+  return align256((size_t)n * kHidden * 2) + qkv_region_bytes(n) + align256((size_t)n * kWOutCols * 2) +
+         align256((size_t)n * kWOutCols) + 2 * align256((size_t)n * 4);
 }
 
 BlockWs carve_block_ws(void* ws, int n) {
@@ -87,13 +93,26 @@ BlockWs carve_block_ws(void* ws, int n) {
   w.qkv_bytes = qkv_region_bytes(n);
   p += w.qkv_bytes;
   w.cat = (bf16*)p;
+  p += align256((size_t)n * kWOutCols * 2);
+  w.cat8 = (uint8_t*)p;
+  p += align256((size_t)n * kWOutCols);
+  w.scale_in = (float*)p;
+  p += align256((size_t)n * 4);
+  w.scale_out = (float*)p;
   return w;
 }
 
 int check_block_weights(const flux3_block_weights* w) {
   REQUIRE(w != nullptr, FLUX3_EINVAL, "block weights are null");
-  REQUIRE_PTR(w->w_in);
-  REQUIRE_PTR(w->w_out);
+  if (w->w_in_fp8 || w->w_out_fp8) {
+    REQUIRE_PTR(w->w_in_fp8);
+    REQUIRE_PTR(w->w_in_scale);
+    REQUIRE_PTR(w->w_out_fp8);
+    REQUIRE_PTR(w->w_out_scale);
+  } else {
+    REQUIRE_PTR(w->w_in);
+    REQUIRE_PTR(w->w_out);
+  }
   REQUIRE_PTR(w->q_scale);
   REQUIRE_PTR(w->k_scale);
   return FLUX3_OK;
@@ -146,10 +165,33 @@ void out_proj(const bf16* cat, int n, const bf16* w_out, float* x, const SegTabl
 void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* mod,
                              const flux3_block_weights* w, const float* table, const BlockWs& ws,
                              hipStream_t st, const SegTable* attn = nullptr) {
-  // a3: h = (1 + scale) LN(x) + shift
-  launch_ln_modulate(x, kHidden, ws.xm, kHidden, n, seg, mod, 3 * kHidden, st);
-  // a4 + a5: q | k | v into qkv; SwiGLU output into the last 9216 columns of cat
-  in_proj(ws.xm, n, B(w->w_in), ws.qkv, ws.cat + kHidden, kWOutCols, st);
+  const bool fp8 = w->w_in_fp8 != nullptr;
+  uint8_t* const xm8 = (uint8_t*)ws.xm;
+  if (fp8) {
+    // a3 with the rowwise FP8 quantization fused; a4 + a5 as an fp8r product
+    launch_ln_modulate_fp8(x, kHidden, xm8, kHidden, ws.scale_in, n, seg, mod, 3 * kHidden, st);
+    GemmArgs g{};
+    g.A8 = xm8;
+    g.lda = kHidden;
+    g.B8 = w->w_in_fp8;
+    g.ldb = kHidden;
+    g.a_scale = ws.scale_in;
+    g.w_scale = w->w_in_scale;
+    g.M = n;
+    g.N = kWInRows;
+    g.K = kHidden;
+    g.epi = GemmEpi::kInProj;
+    g.C = ws.qkv;
+    g.ldc = 3 * kHidden;
+    g.H = ws.cat + kHidden;
+    g.ldh = kWOutCols;
+    launch_gemm_fp8(g, st);
+  } else {
+    // a3: h = (1 + scale) LN(x) + shift
+    launch_ln_modulate(x, kHidden, ws.xm, kHidden, n, seg, mod, 3 * kHidden, st);
+    // a4 + a5: q | k | v into qkv; SwiGLU output into the last 9216 columns of cat
+    in_proj(ws.xm, n, B(w->w_in), ws.qkv, ws.cat + kHidden, kWOutCols, st);
+  }
   // a6: RMSNorm + RoPE on q and k
   launch_qk_norm_rope(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, n, B(w->q_scale),
                       B(w->k_scale), table, st);
@@ -163,7 +205,31 @@ void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
                      ws.cat + (size_t)r0 * kWOutCols, kWOutCols, r1 - r0, st);
   }
   // a8: gated residual
-  out_proj(ws.cat, n, B(w->w_out), x, seg, mod, st, ws.qkv, ws.qkv_bytes);
+  if (fp8) {
+    launch_quant_rows_fp8(ws.cat, kWOutCols, n, kWOutCols, ws.cat8, kWOutCols, ws.scale_out, st);
+    GemmArgs o{};
+    o.A8 = ws.cat8;
+    o.lda = kWOutCols;
+    o.B8 = w->w_out_fp8;
+    o.ldb = kWOutCols;
+    o.a_scale = ws.scale_out;
+    o.w_scale = w->w_out_scale;
+    o.M = n;
+    o.N = kHidden;
+    o.K = kWOutCols;
+    o.epi = GemmEpi::kGatedResidual;
+    o.C = x;
+    o.ldc = kHidden;
+    o.mod = mod;
+    o.mod_stride = 3 * kHidden;
+    o.gate_offset = 2 * kHidden;
+    o.seg = seg;
+    o.split_ws = ws.qkv;
+    o.split_ws_bytes = ws.qkv_bytes;
+    launch_gemm_fp8(o, st);
+  } else {
+    out_proj(ws.cat, n, B(w->w_out), x, seg, mod, st, ws.qkv, ws.qkv_bytes);
+  }
 }
 
 }  // namespace
@@ -379,6 +445,65 @@ int flux3_block_forward(float* x, int n, const int* seg_off, int n_seg, const fl
           block_ws_bytes(n));
   block_forward_unchecked(x, n, seg, mod, w, table, carve_block_ws(workspace, n), stream);
   return check_launch("block_forward");
+}
+
+int flux3_quantize_rows_fp8(const uint16_t* x, int ldx, int rows, int cols, uint8_t* q, int ldq,
+                            float* scale, hipStream_t stream) {
+  REQUIRE(rows >= 0 && cols > 0 && cols % 8 == 0, FLUX3_EINVAL, "rows=%d cols=%d", rows, cols);
+  if (rows == 0) return FLUX3_OK;
+  REQUIRE_PTR(x);
+  REQUIRE(q != nullptr, FLUX3_EINVAL, "q is null");
+  REQUIRE(scale != nullptr, FLUX3_EINVAL, "scale is null");
+  REQUIRE_LD(ldx, cols);
+  REQUIRE(ldq >= cols && ldq % 8 == 0 && ((uintptr_t)q & 7) == 0, FLUX3_EINVAL,
+          "ldq=%d must be >= cols and a multiple of 8 (q 8-byte aligned)", ldq);
+  launch_quant_rows_fp8(B(x), ldx, rows, cols, q, ldq, scale, stream);
+  return check_launch("quantize_rows_fp8");
+}
+
+int flux3_pack_block_fp8(const uint16_t* w_in, const uint16_t* w_out, uint8_t* w_in_fp8,
+                         float* w_in_scale, uint8_t* w_out_fp8, float* w_out_scale, hipStream_t stream) {
+  REQUIRE_PTR(w_in);
+  REQUIRE_PTR(w_out);
+  REQUIRE_PTR(w_in_fp8);
+  REQUIRE_PTR(w_out_fp8);
+  REQUIRE(w_in_scale != nullptr && w_out_scale != nullptr, FLUX3_EINVAL, "scale buffers are null");
+  launch_quant_rows_fp8(B(w_in), kHidden, kWInRows, kHidden, w_in_fp8, kHidden, w_in_scale, stream);
+  launch_quant_rows_fp8(B(w_out), kWOutCols, kHidden, kWOutCols, w_out_fp8, kWOutCols, w_out_scale, stream);
+  return check_launch("pack_block_fp8");
+}
+
+int flux3_linear_fp8(const uint8_t* a, int lda, const float* a_scale, const uint8_t* w, int ldw,
+                     const float* w_scale, uint16_t* y, float* y_f32, int ldy, int m, int n, int k,
+                     hipStream_t stream) {
+  REQUIRE(m >= 0, FLUX3_EINVAL, "m=%d", m);
+  if (m == 0) return FLUX3_OK;
+  REQUIRE(gemm_fp8_shape_ok(m, n, k), FLUX3_EUNSUPPORTED,
+          "fp8 product needs n %% 256 == 0, k %% 128 == 0, k >= 256 (m=%d n=%d k=%d)", m, n, k);
+  REQUIRE_PTR(a);
+  REQUIRE_PTR(w);
+  REQUIRE(a_scale != nullptr && w_scale != nullptr, FLUX3_EINVAL, "scales are null");
+  REQUIRE(lda >= k && lda % 16 == 0 && ldw >= k && ldw % 16 == 0, FLUX3_EINVAL,
+          "lda=%d ldw=%d must be >= k and multiples of 16", lda, ldw);
+  REQUIRE((y == nullptr) != (y_f32 == nullptr), FLUX3_EINVAL, "give exactly one of y, y_f32");
+  REQUIRE(y == nullptr || aligned16(y), FLUX3_EINVAL, "y misaligned");
+  REQUIRE(y_f32 == nullptr || aligned16(y_f32), FLUX3_EINVAL, "y_f32 misaligned");
+  REQUIRE(ldy >= n && ldy % 8 == 0, FLUX3_EINVAL, "ldy=%d", ldy);
+  GemmArgs g{};
+  g.A8 = a;
+  g.lda = lda;
+  g.B8 = w;
+  g.ldb = ldw;
+  g.a_scale = a_scale;
+  g.w_scale = w_scale;
+  g.M = m;
+  g.N = n;
+  g.K = k;
+  g.epi = y ? GemmEpi::kStoreBf16 : GemmEpi::kStoreF32;
+  g.C = y ? (void*)y : (void*)y_f32;
+  g.ldc = ldy;
+  launch_gemm_fp8(g, stream);
+  return check_launch("linear_fp8");
 }
 
 // ---- conditioning and the whole stack -----------------------------------------------

@@ -9,6 +9,7 @@
 //     the block's output (same sections: gated residual).
 // The kernels themselves are in gemm_kernels.hpp.
 #include "gemm_kernels.hpp"
+#include "gemm_fp8.hpp"
 
 #include <algorithm>
 
@@ -113,7 +114,69 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(float* x, int ldx, co
   *xp = xv;
 }
 
+// fp8 products: the persistent ring kernel with 4 slices of 64 fp8 in flight.
+constexpr int kFp8Stages = 4;
+
+template <GemmEpi EPI>
+void launch_ring_fp8(const GemmArgs& g, hipStream_t st) {
+  const int tiles_m = (g.M + 255) / 256;
+  const int tiles_n = g.N / 256;
+  const int items = tiles_m * tiles_n * (EPI == GemmEpi::kSplitPartial ? g.ksplit : 1);
+  const int grid = std::min(items, cu_count());
+  hipLaunchKernelGGL((gemm::gemm_ring_fp8_kernel<kFp8Stages, EPI>), dim3(grid), dim3(256), 0, st, g,
+                     tiles_m, tiles_n);
+}
+
+// K ranges of a split fp8 product: the largest divisor s of K/128 with
+// s * tiles <= CUs and ranges of at least two 128-wide units (the ring needs
+// an even number of slices, at least as many as its stages); 1 when the
+// product already has 128 tiles or more.
+int split_count_fp8(int m, int n, int k) {
+  const long tiles = (long)((m + 255) / 256) * (n / 256);
+  if (tiles >= 128) return 1;
+  const int ku = k / 128;
+  int best = 1;
+  for (int s = 2; s <= ku / 2; ++s)
+    if (ku % s == 0 && tiles * s <= cu_count()) best = s;
+  return best;
+}
+
 }  // namespace
+
+bool gemm_fp8_shape_ok(int m, int n, int k) {
+  return m > 0 && n > 0 && n % 256 == 0 && k % 128 == 0 && k / 64 >= kFp8Stages;
+}
+
+// C = (A8 B8^T) * a_scale[row] * w_scale[col] with the epilogue g.epi; the
+// host has checked gemm_fp8_shape_ok and 16-byte row alignment.
+void launch_gemm_fp8(const GemmArgs& g, hipStream_t st) {
+  if (g.M <= 0) return;
+  const bool gated = g.epi == GemmEpi::kGatedResidual;
+  if ((gated || g.epi == GemmEpi::kStoreF32) && g.split_ws != nullptr) {
+    const int s = split_count_fp8(g.M, g.N, g.K);
+    if (s > 1 && split_bytes(g.M, g.N, s) <= g.split_ws_bytes) {
+      GemmArgs h = g;
+      h.epi = GemmEpi::kSplitPartial;
+      h.ksplit = s;
+      h.C = g.split_ws;
+      h.ldc = g.N;
+      launch_ring_fp8<GemmEpi::kSplitPartial>(h, st);
+      const size_t stride = (size_t)((g.M + 255) / 256) * 256 * g.N;
+      const size_t quads = (size_t)g.M * (g.N / 4);
+      hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st,
+                         (float*)g.C, g.ldc, (const float*)g.split_ws, stride, s, g.M, g.N,
+                         gated ? g.mod : nullptr, g.mod_stride, g.gate_offset, g.seg);
+      return;
+    }
+  }
+  switch (g.epi) {
+    case GemmEpi::kStoreBf16: launch_ring_fp8<GemmEpi::kStoreBf16>(g, st); break;
+    case GemmEpi::kStoreF32: launch_ring_fp8<GemmEpi::kStoreF32>(g, st); break;
+    case GemmEpi::kInProj: launch_ring_fp8<GemmEpi::kInProj>(g, st); break;
+    case GemmEpi::kGatedResidual: launch_ring_fp8<GemmEpi::kGatedResidual>(g, st); break;
+    case GemmEpi::kSplitPartial: break;
+  }
+}
 
 size_t gemm_split_ws_bytes(int m, int n, int k) {
   const int s = split_count(m, n, k);

@@ -132,12 +132,33 @@ struct TileWalk {
 // address arithmetic is hoisted into the surrounding tile loop to hold a
 // register there, and scheduling fences after each fragment keep the
 // accumulator reads of one fragment together.
-template <class T, GemmEpi EPI>
+//
+// SC (fp8 products): every value is first scaled by its row's and column's
+// scale, read from LDS (sc: the wave's 128 row scales, then at sc + 128 its
+// 128 column scales); LDS reads wait on lgkmcnt, not on the stores in flight.
+template <class T, GemmEpi EPI, bool SC = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::FM][T::FN],
-                                         int wrow0, int wcol0) {
+                                         int wrow0, int wcol0, const float* sc = nullptr) {
   int lane;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
   const int lr = lane & 31;
+  // Fragment (i, j), register group g4, with the fp8 scales applied.
+  auto f4 = [&](int i, int j, int g4, float sa) -> float4 {
+    float4 v = make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                           acc[i][j][4 * g4 + 3]);
+    if constexpr (SC) {
+      const float4 w = *(const float4*)(sc + 128 + 32 * j + frag_col(g4, lane));
+      v.x *= sa * w.x;
+      v.y *= sa * w.y;
+      v.z *= sa * w.z;
+      v.w *= sa * w.w;
+    }
+    return v;
+  };
+  auto row_scale = [&](int i) -> float {
+    if constexpr (SC) return sc[32 * i + lr];
+    else return 1.f;
+  };
   if constexpr (EPI == GemmEpi::kStoreBf16 || EPI == GemmEpi::kInProj) {
     if (EPI == GemmEpi::kStoreBf16 || wcol0 < 3 * kHidden) {
       bf16* C = (bf16*)g.C;
@@ -145,14 +166,18 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::F
       for (int i = 0; i < T::FM; ++i) {
         const int row = wrow0 + 32 * i + lr;
         if (row < g.M) {
+          const float sa = row_scale(i);
           bf16* crow = C + (size_t)row * g.ldc + wcol0;
 #pragma unroll
           for (int j = 0; j < T::FN; ++j) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
+              const float4 f = f4(i, j, g4, sa);
               bf16x4 v;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = to_bf16(acc[i][j][4 * g4 + e]);
+              v[0] = to_bf16(f.x);
+              v[1] = to_bf16(f.y);
+              v[2] = to_bf16(f.z);
+              v[3] = to_bf16(f.w);
               *(bf16x4*)(crow + 32 * j + frag_col(g4, lane)) = v;
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -167,17 +192,18 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::F
       for (int i = 0; i < T::FM; ++i) {
         const int row = wrow0 + 32 * i + lr;
         if (row < g.M) {
+          const float sa = row_scale(i);
           bf16* hrow = g.H + (size_t)row * g.ldh + hcol0;
 #pragma unroll
           for (int p = 0; p < T::FN / 2; ++p) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
+              const float4 a = f4(i, 2 * p, g4, sa), b = f4(i, 2 * p + 1, g4, sa);
               bf16x4 v;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float a = acc[i][2 * p][4 * g4 + e], b = acc[i][2 * p + 1][4 * g4 + e];
-                v[e] = to_bf16(silu_f(a) * b);
-              }
+              v[0] = to_bf16(silu_f(a.x) * b.x);
+              v[1] = to_bf16(silu_f(a.y) * b.y);
+              v[2] = to_bf16(silu_f(a.z) * b.z);
+              v[3] = to_bf16(silu_f(a.w) * b.w);
               *(bf16x4*)(hrow + 32 * p + frag_col(g4, lane)) = v;
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -191,14 +217,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::F
     for (int i = 0; i < T::FM; ++i) {
       const int row = wrow0 + 32 * i + lr;
       if (row < g.M) {
+        const float sa = row_scale(i);
         float* crow = C + (size_t)row * g.ldc + wcol0;
 #pragma unroll
         for (int j = 0; j < T::FN; ++j)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4)
-            *(float4*)(crow + 32 * j + frag_col(g4, lane)) =
-                make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
-                            acc[i][j][4 * g4 + 3]);
+            *(float4*)(crow + 32 * j + frag_col(g4, lane)) = f4(i, j, g4, sa);
       }
     }
   } else if constexpr (EPI == GemmEpi::kSplitPartial) {
@@ -207,14 +232,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::F
     float* C = (float*)g.C;
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
+      const float sa = row_scale(i);
       float* crow = C + (size_t)(wrow0 + 32 * i + lr) * g.ldc + wcol0;
 #pragma unroll
       for (int j = 0; j < T::FN; ++j)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
-          *(float4*)(crow + 32 * j + frag_col(g4, lane)) =
-              make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
-                          acc[i][j][4 * g4 + 3]);
+          *(float4*)(crow + 32 * j + frag_col(g4, lane)) = f4(i, j, g4, sa);
     }
   } else {
     static_assert(EPI == GemmEpi::kGatedResidual, "epilogue kind");
@@ -224,6 +248,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::F
     for (int i = 0; i < T::FM; ++i) {
       const int row = wrow0 + 32 * i + lr;
       if (row < g.M) {
+        const float sa = row_scale(i);
         const float* __restrict__ gate =
             g.mod + (size_t)seg_of_row(g.seg, row) * g.mod_stride + g.gate_offset + wcol0;
         float* __restrict__ xrow = (float*)g.C + (size_t)row * g.ldc + wcol0;
@@ -239,11 +264,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::F
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int c = 32 * j + frag_col(g4, lane);
+            const float4 f = f4(i, j, g4, sa);
             float4 r = xv[g4];
-            r.x += gt[g4].x * acc[i][j][4 * g4];
-            r.y += gt[g4].y * acc[i][j][4 * g4 + 1];
-            r.z += gt[g4].z * acc[i][j][4 * g4 + 2];
-            r.w += gt[g4].w * acc[i][j][4 * g4 + 3];
+            r.x += gt[g4].x * f.x;
+            r.y += gt[g4].y * f.y;
+            r.z += gt[g4].z * f.z;
+            r.w += gt[g4].w * f.w;
             *(float4*)(xrow + c) = r;
           }
           __builtin_amdgcn_sched_barrier(0);

@@ -48,11 +48,25 @@ struct GemmArgs {
   size_t split_ws_bytes;
   // kSplitPartial: number of K ranges (divides K / 32)
   int ksplit;
+  // fp8 products (gemm_fp8.hip): A8 [M][lda], B8 [N][ldb] E4M3 codes; the
+  // product of row r and column c is scaled by a_scale[r] * w_scale[c].
+  const uint8_t* A8;
+  const uint8_t* B8;
+  const float* a_scale;
+  const float* w_scale;
 };
 
 // Scratch bytes a kGatedResidual or kStoreF32 product of this shape uses when
 // split over K (0: it is not split).
 size_t gemm_split_ws_bytes(int m, int n, int k);
+
+// fp8 (E4M3, rowwise-scaled) products: shapes the kernel takes, and launch.
+bool gemm_fp8_shape_ok(int m, int n, int k);
+void launch_gemm_fp8(const GemmArgs& g, hipStream_t st);
+void launch_ln_modulate_fp8(const float* x, int ldx, uint8_t* out, int ldo, float* scale, int n,
+                            const SegTable& seg, const float* mod, int mod_stride, hipStream_t st);
+void launch_quant_rows_fp8(const bf16* x, int ldx, int rows, int cols, uint8_t* out, int ldo,
+                           float* scale, hipStream_t st);
 
 void launch_ln_modulate(const float* x, int ldx, bf16* out, int ldo, int n, const SegTable& seg,
                         const float* mod, int mod_stride, hipStream_t st);

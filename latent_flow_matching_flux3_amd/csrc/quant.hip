@@ -1,0 +1,148 @@
+// Rowwise FP8 quantization for the fp8r projections ("Welcome FLUX.3 Image
+// Klein in Diffusers", §Base model and quantized variants: fp8r, rowwise
+// FP8): per row, scale = max|x| / 448 and E4M3 codes of x * (448 / max|x|),
+// the scale, its inverse and the product in fp32; codes by the hardware
+// conversion (OCP E4M3, round to nearest even); a row of zeros gets scale 1.
+//   - ln_modulate_fp8_kernel: LayerNorm + modulation (as ln_modulate_kernel)
+//     with the quantization of the modulated row fused (the in-projection's
+//     input never exists in bf16);
+//   - quant_rows_fp8_kernel: any bf16 rows (weights once; the
+//     out-projection's input [o | h] every block).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace flux3 {
+
+namespace {
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// Four values scaled by inv, as four E4M3 codes in one dword (byte e = value e).
+__device__ __forceinline__ unsigned fp8x4(float a, float b, float c, float d, float inv) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a * inv, b * inv, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c * inv, d * inv, w, true);
+  return (unsigned)w;
+}
+
+// scale = amax / 448 and its inverse 448 / amax (IEEE fp32 divisions).
+__device__ __forceinline__ void row_scale(float amax, float& scale, float& inv) {
+  if (amax > 0.f) {
+    scale = amax / 448.0f;
+    inv = 448.0f / amax;
+  } else {
+    scale = 1.f;
+    inv = 1.f;
+  }
+}
+
+constexpr int kLnRowsPerBlock = 4;
+
+// One wave per row of the fp32 residual stream (3072 values, 48 per lane in
+// registers); out: [n][ldo] codes, scale: [n] fp32.
+__global__ __launch_bounds__(256) void ln_modulate_fp8_kernel(const float* __restrict__ x, int ldx,
+                                                              uint8_t* __restrict__ out, int ldo,
+                                                              float* __restrict__ out_scale, int n,
+                                                              SegTable seg,
+                                                              const float* __restrict__ mod,
+                                                              int mod_stride) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kLnRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const float* xr = x + (size_t)row * ldx;
+  float v[12][4];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    const float4 c = *(const float4*)(xr + (lane + 64 * i) * 4);
+    v[i][0] = c.x;
+    v[i][1] = c.y;
+    v[i][2] = c.z;
+    v[i][3] = c.w;
+    s += (c.x + c.y) + (c.z + c.w);
+  }
+  const float mu = wave_sum(s) * (1.0f / kHidden);
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < 12; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float d = v[i][e] - mu;
+      q += d * d;
+    }
+  const float var = wave_sum(q) * (1.0f / kHidden);
+  const float rstd = 1.0f / sqrtf(var + 1e-6f);
+  const float* shift = mod + (size_t)seg_of_row(seg, row) * mod_stride;
+  const float* scale = shift + kHidden;
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    const int c0 = (lane + 64 * i) * 4;
+    const float4 sh = *(const float4*)(shift + c0);
+    const float4 sc = *(const float4*)(scale + c0);
+    v[i][0] = (1.0f + sc.x) * ((v[i][0] - mu) * rstd) + sh.x;
+    v[i][1] = (1.0f + sc.y) * ((v[i][1] - mu) * rstd) + sh.y;
+    v[i][2] = (1.0f + sc.z) * ((v[i][2] - mu) * rstd) + sh.z;
+    v[i][3] = (1.0f + sc.w) * ((v[i][3] - mu) * rstd) + sh.w;
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])), fmaxf(fabsf(v[i][2]), fabsf(v[i][3]))));
+  }
+  float rs, inv;
+  row_scale(wave_max(amax), rs, inv);
+  uint8_t* orow = out + (size_t)row * ldo;
+#pragma unroll
+  for (int i = 0; i < 12; ++i)
+    *(unsigned*)(orow + (lane + 64 * i) * 4) = fp8x4(v[i][0], v[i][1], v[i][2], v[i][3], inv);
+  if (lane == 0) out_scale[row] = rs;
+}
+
+// One workgroup per row of `cols` bf16 values (cols a multiple of 8): the
+// row max in a first pass, the codes in a second (the row is in cache).
+__global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const bf16* __restrict__ x, int ldx,
+                                                             int cols, uint8_t* __restrict__ out,
+                                                             int ldo, float* __restrict__ out_scale) {
+  __shared__ float part[4];
+  const int row = blockIdx.x;
+  const bf16* xr = x + (size_t)row * ldx;
+  float amax = 0.f;
+  for (int c = threadIdx.x * 8; c < cols; c += 256 * 8) {
+    const bf16x8 t = *(const bf16x8*)(xr + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(to_f32(t[e])));
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+  float rs, inv;
+  row_scale(amax, rs, inv);
+  uint8_t* orow = out + (size_t)row * ldo;
+  for (int c = threadIdx.x * 8; c < cols; c += 256 * 8) {
+    const bf16x8 t = *(const bf16x8*)(xr + c);
+    uint2 w;
+    w.x = fp8x4(to_f32(t[0]), to_f32(t[1]), to_f32(t[2]), to_f32(t[3]), inv);
+    w.y = fp8x4(to_f32(t[4]), to_f32(t[5]), to_f32(t[6]), to_f32(t[7]), inv);
+    *(uint2*)(orow + c) = w;
+  }
+  if (threadIdx.x == 0) out_scale[row] = rs;
+}
+
+}  // namespace
+
+void launch_ln_modulate_fp8(const float* x, int ldx, uint8_t* out, int ldo, float* scale, int n,
+                            const SegTable& seg, const float* mod, int mod_stride, hipStream_t st) {
+  if (n <= 0) return;
+  dim3 grid((n + kLnRowsPerBlock - 1) / kLnRowsPerBlock);
+  hipLaunchKernelGGL(ln_modulate_fp8_kernel, grid, dim3(256), 0, st, x, ldx, out, ldo, scale, n, seg,
+                     mod, mod_stride);
+}
+
+void launch_quant_rows_fp8(const bf16* x, int ldx, int rows, int cols, uint8_t* out, int ldo,
+                           float* scale, hipStream_t st) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3(rows), dim3(256), 0, st, x, ldx, cols, out, ldo, scale);
+}
+
+}  // namespace flux3

@@ -388,7 +388,8 @@ def _early_prefix(mode: str, i: int) -> str:
 
 
 def stack_forward(W, B, img: np.ndarray, cond, txt: np.ndarray, img_h: int, img_w: int,
-                  refs, sigma: float, sigma_next, n_early: int = 5, n_single: int = 28) -> np.ndarray:
+                  refs, sigma: float, sigma_next, n_early: int = 5, n_single: int = 28,
+                  block=None) -> np.ndarray:
     """Velocity for the image tokens ([blog] §Two stages, §Every token gets its
     own timestep; [issue] Structure):
       1. embed: img emb_in.image, references emb_in.image_cond, text txt_in;
@@ -399,9 +400,11 @@ def stack_forward(W, B, img: np.ndarray, cond, txt: np.ndarray, img_h: int, img_
          single_stream_modulations;
       5. final layer on the image tokens -> v [N_img, 128].
     W(name) -> float64 global tensor; B(prefix) -> dict of one block's float64
-    tensors.  cond may be None (no references)."""
+    tensors.  cond may be None (no references).  block: the block function
+    (block_forward, or block_forward_fp8r for the fp8r transformer)."""
+    block = block_forward if block is None else block
     ids = build_ids(img_h, img_w, txt.shape[0], refs)
-    modes, streams, vecs = stage1(W, B, img, cond, txt, ids, refs, sigma, sigma_next, n_early)
+    modes, streams, vecs = stage1(W, B, img, cond, txt, ids, refs, sigma, sigma_next, n_early, block)
 
     # stage 2: the streams concatenated, every token attends to every token
     seg = []
@@ -413,14 +416,14 @@ def stack_forward(W, B, img: np.ndarray, cond, txt: np.ndarray, img_h: int, img_
     mods = np.stack([modulation(vecs[m], W(f"single_stream_modulations.{m}.lin.weight"))
                      for m in modes])
     for i in range(n_single):
-        x = block_forward(x, seg, mods, B(f"single_blocks.{i}"), ids)
+        x = block(x, seg, mods, B(f"single_blocks.{i}"), ids)
 
     n_img = img.shape[0]
     return final_layer(x[:n_img], vecs["image"], W("final_layer.image.adaLN_modulation.1.weight"),
                        W("final_layer.image.linear.weight"))
 
 
-def stage1(W, B, img, cond, txt, ids, refs, sigma, sigma_next, n_early: int = 5):
+def stage1(W, B, img, cond, txt, ids, refs, sigma, sigma_next, n_early: int = 5, block=None):
     """Embedding and stage 1 ([blog] §Two stages; [issue] Structure): each
     mode is embedded by its own input linear, then runs through its own
     n_early blocks with its early_stream_modulations, attending only to its
@@ -439,7 +442,7 @@ def stage1(W, B, img, cond, txt, ids, refs, sigma, sigma_next, n_early: int = 5)
         ids_m = ids[start:start + n]
         mod = modulation(vecs[m], W(f"early_stream_modulations.{m}.lin.weight"))[None]
         for i in range(n_early):
-            xs = block_forward(xs, [(0, n)], mod, B(_early_prefix(m, i)), ids_m)
+            xs = (block or block_forward)(xs, [(0, n)], mod, B(_early_prefix(m, i)), ids_m)
         streams.append(xs)
         start += n
     return modes, streams, vecs

@@ -13,6 +13,13 @@ import flux3_synth as syn
 # max |err| <= 2e-2 * max |ref|.
 COS_MIN = 0.9995
 REL_MAX = 2e-2
+# fp8r outputs (rowwise E4M3 projections): the kernel quantizes activations it
+# computed in fp32 (and [o | h] after bf16 rounding), the oracle its float64
+# values, so codes near a rounding boundary can land one E4M3 step (2^-3 of
+# the element) apart: about 1/64 of a row's inputs at bf16-level input
+# differences, moving an output by ~0.75% of its rms; the maximum over ~1e5
+# outputs lies a few times above that.  Same cosine bar.
+FP8_REL_MAX = 5e-2
 
 
 def require_gpu():

@@ -24,9 +24,10 @@ def L():
 class Weights:
     """Seeded weights: device copies for the library, float64 views for the oracle."""
 
-    def __init__(self, L, seed, lay, n_early, n_single, base=False):
-        """base: the base checkpoint's tensor set (no ref_time_in)."""
+    def __init__(self, L, seed, lay, n_early, n_single, base=False, fp8=False):
+        """base: the base checkpoint's tensor set (no ref_time_in); fp8: fp8r blocks."""
         self.seed = seed
+        self.fp8 = fp8
         self.glob_cpu = {k: syn.global_weight(seed, k) for k in syn.GLOBAL_SHAPES
                          if not (base and k.startswith("ref_time_in."))}
         glob = {k: dev(v) for k, v in self.glob_cpu.items()}
@@ -40,7 +41,7 @@ class Weights:
 
     def _packed(self, L, prefix):
         w = {k: dev(v) for k, v in syn.block_weights(self.seed, prefix).items()}
-        b = L.PackedBlock(w)
+        b = L.PackedBlock(w, fp8=self.fp8)
         torch.cuda.synchronize()
         return b
 
@@ -298,3 +299,31 @@ def test_sample_cfg(L):
     assert torch.equal(x, xs), "flux3_sample_cfg differs from the step-by-step loop"
     xr = O.sample_base_cfg(_oracle_velocity(wts, lay, None, [txt0, txt1], 1, 1), f64(img), steps, g)
     assert_agree(f64(x), xr, f"cfg sampler {steps} steps")
+
+
+def test_stack_fp8r(L):
+    """The whole transformer (reduced depth, real widths, references) with
+    fp8r blocks against the oracle's stack with fp8r blocks."""
+    from gpu_util import FP8_REL_MAX
+    lay = syn.Layout(6, 6, 40, [(4, 5)])
+    seed = 350
+    say(f"stack fp8r n={lay.n_total} depth 1+2")
+    wts = Weights(L, seed, lay, 1, 2, fp8=True)
+    img, cond, txt = _inputs(lay, seed)
+    sig, sig_next = np.float32(0.8739), np.float32(0.6979)
+    v = _gpu_stack(L, wts, lay, img, cond, txt, float(sig), float(sig_next))
+    args = (wts.W, wts.B, f64(img), f64(cond), f64(txt), lay.img_h, lay.img_w, lay.refs,
+            float(sig), float(sig_next), 1, 2)
+    ref = O.stack_forward(*args, block=O.block_forward_fp8r)
+    plain = O.stack_forward(*args)
+    from gpu_util import agreement
+    c_gpu, r_gpu = agreement(f64(v), ref)
+    c_q, r_q = agreement(ref, plain)
+    say(f"  stack fp8r: gpu vs oracle fp8r cos={c_gpu:.7f} rel={r_gpu:.3e}; "
+        f"oracle fp8r vs oracle unquantized cos={c_q:.7f} rel={r_q:.3e}")
+    # The kernel and the oracle quantize activations computed in different
+    # precision, so their FP8 codes differ at rounding boundaries and the
+    # differences compound through the blocks: the GPU result must be closer
+    # to the oracle's fp8r result than FP8 quantization itself moves it.
+    assert 1 - c_gpu <= 1 - c_q and r_gpu <= r_q, (c_gpu, r_gpu, c_q, r_q)
+    assert_agree(f64(v), ref, "stack fp8r", cos_min=0.999, rel_max=FP8_REL_MAX)
