@@ -6,8 +6,10 @@
 //   - ln_modulate_fp8_kernel: LayerNorm + modulation (as ln_modulate_kernel)
 //     with the quantization of the modulated row fused (the in-projection's
 //     input never exists in bf16);
-//   - quant_rows_fp8_kernel: any bf16 rows (weights once; the
-//     out-projection's input [o | h] every block).
+//   - quant_rows_fp8_reg_kernel: rows of a multiple of 2048 values up to
+//     16384 (the out-projection's input [o | h], 12288 wide, every block),
+//     read once into registers;
+//   - quant_rows_fp8_kernel: any other width (the weights, once), two passes.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -129,6 +131,43 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const bf16* __restr
   if (threadIdx.x == 0) out_scale[row] = rs;
 }
 
+// One workgroup per row of C * 2048 bf16 values, the row in registers (C
+// 16-byte chunks per thread): one read of the row.
+template <int C>
+__global__ __launch_bounds__(256) void quant_rows_fp8_reg_kernel(const bf16* __restrict__ x, int ldx,
+                                                                 uint8_t* __restrict__ out, int ldo,
+                                                                 float* __restrict__ out_scale) {
+  __shared__ float part[4];
+  const int row = blockIdx.x;
+  const bf16* xr = x + (size_t)row * ldx;
+  float v[C][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    const bf16x8 t = *(const bf16x8*)(xr + (threadIdx.x + 256 * i) * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[i][e] = to_f32(t[e]);
+      amax = fmaxf(amax, fabsf(v[i][e]));
+    }
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+  float rs, inv;
+  row_scale(amax, rs, inv);
+  uint8_t* orow = out + (size_t)row * ldo;
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    uint2 w;
+    w.x = fp8x4(v[i][0], v[i][1], v[i][2], v[i][3], inv);
+    w.y = fp8x4(v[i][4], v[i][5], v[i][6], v[i][7], inv);
+    *(uint2*)(orow + (threadIdx.x + 256 * i) * 8) = w;
+  }
+  if (threadIdx.x == 0) out_scale[row] = rs;
+}
+
 }  // namespace
 
 void launch_ln_modulate_fp8(const float* x, int ldx, uint8_t* out, int ldo, float* scale, int n,
@@ -142,6 +181,25 @@ void launch_ln_modulate_fp8(const float* x, int ldx, uint8_t* out, int ldo, floa
 void launch_quant_rows_fp8(const bf16* x, int ldx, int rows, int cols, uint8_t* out, int ldo,
                            float* scale, hipStream_t st) {
   if (rows <= 0) return;
+#define FLUX3_QUANT_REG(C)                                                                            \
+  case C:                                                                                             \
+    hipLaunchKernelGGL(quant_rows_fp8_reg_kernel<C>, dim3(rows), dim3(256), 0, st, x, ldx, out, ldo, \
+                       scale);                                                                        \
+    return;
+  if (cols % 2048 == 0) {
+    switch (cols / 2048) {
+      FLUX3_QUANT_REG(1)
+      FLUX3_QUANT_REG(2)
+      FLUX3_QUANT_REG(3)
+      FLUX3_QUANT_REG(4)
+      FLUX3_QUANT_REG(5)
+      FLUX3_QUANT_REG(6)
+      FLUX3_QUANT_REG(7)
+      FLUX3_QUANT_REG(8)
+      default: break;
+    }
+  }
+#undef FLUX3_QUANT_REG
   hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3(rows), dim3(256), 0, st, x, ldx, cols, out, ldo, scale);
 }
 

@@ -18,10 +18,11 @@ def L():
     return require_gpu()
 
 
-@pytest.mark.parametrize("rows,cols", [(7, 264), (33, 3072), (5, 12288)])
+@pytest.mark.parametrize("rows,cols", [(7, 264), (33, 3072), (5, 12288), (9, 2048), (3, 16384)])
 def test_quantize_rows_bit_exact(L, rows, cols):
     """Codes and scales equal the oracle's (both decide in fp32), incl. a
-    zero row and rows of very different magnitudes."""
+    zero row and rows of very different magnitudes; widths of both the
+    register (multiples of 2048) and the two-pass kernel."""
     g = torch.Generator().manual_seed(rows * cols)
     x = torch.randn(rows, cols, generator=g) * torch.exp2(torch.randint(-10, 10, (rows, 1), generator=g).float())
     x[min(3, rows - 1)] = 0
