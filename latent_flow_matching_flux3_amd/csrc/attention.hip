@@ -34,6 +34,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace flux3 {
 
 namespace {
@@ -117,22 +119,54 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
   }
 
   // Tile loads: each wave fills 2 KiB of K and 2 KiB of V per tile, 1 KiB
-  // (4 key rows) per global_load_lds; lane t lands at row t/16, physical chunk
-  // t%16 and so fetches the logical chunk that maps there.
+  // (4 key rows) per global_load_lds_dwordx4; lane t lands at row t/16,
+  // physical chunk t%16 and so fetches the logical chunk that maps there.
+  // The source is a scalar base (the tile's first key row) plus a fixed
+  // 32-bit lane offset; a partial last tile uses lane offsets whose rows are
+  // clamped to the last key.  The loads are inline assembly (m0 set, one wait
+  // state, load; no register results): the explicit waits and barriers below
+  // order them against the LDS reads, and the compiler then adds no waits of
+  // its own.
   const int sub_row = lane >> 4, pchunk = lane & 15;
   constexpr int kBlk = kBKV / 4 / kWaves;  // KiB blocks of K (and of V) per wave per tile
-  auto issue_tile = [&](int tile, int slot) {
-    const int key0 = min(tile, (n - 1) / kBKV) * kBKV;  // a tile past the end reloads the last one
+  const int last_tile = (n - 1) / kBKV;
+  const int last_rows = n - last_tile * kBKV;  // keys in the last tile (1 .. 32)
+  unsigned voff_k[kBlk], voff_v[kBlk], voff_kl[kBlk], voff_vl[kBlk];
 #pragma unroll
-    for (int b = 0; b < kBlk; ++b) {
-      const int row = (wave * kBlk + b) * 4 + sub_row;   // 0..31
-      const int grow = min(key0 + row, n - 1);
-      const int kc = pchunk ^ (row & 15);
-      const int vc = pchunk ^ (4 * (row & 3));
-      __builtin_amdgcn_global_load_lds((const gmem_void_t*)(k + (size_t)grow * ldk + hoff + kc * 8),
-                                       (lds_void_t*)(&ks_lds[slot][(wave * kBlk + b) * 64]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const gmem_void_t*)(v + (size_t)grow * ldv + hoff + vc * 8),
-                                       (lds_void_t*)(&vs_lds[slot][(wave * kBlk + b) * 64]), 16, 0, 0);
+  for (int b = 0; b < kBlk; ++b) {
+    const int row = (wave * kBlk + b) * 4 + sub_row;  // 0..31
+    const int rl = min(row, last_rows - 1);
+    const int kc = pchunk ^ (row & 15);
+    const int vc = pchunk ^ (4 * (row & 3));
+    voff_k[b] = (unsigned)((row * ldk + hoff + kc * 8) * 2);
+    voff_v[b] = (unsigned)((row * ldv + hoff + vc * 8) * 2);
+    voff_kl[b] = (unsigned)((rl * ldk + hoff + kc * 8) * 2);
+    voff_vl[b] = (unsigned)((rl * ldv + hoff + vc * 8) * 2);
+  }
+  const unsigned lds_base = (unsigned)(size_t)(lds_void_t*)ring_lds;
+  auto dma = [&](unsigned voff, const void* base, unsigned dst) __attribute__((always_inline)) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(dst) : "m0");
+  };
+  auto issue_tile = [&](int tile, auto SLOT) __attribute__((always_inline)) {
+    constexpr int slot = decltype(SLOT)::value;
+    const int tt = min(tile, last_tile);  // a tile past the end reloads the last one
+    const char* kb = (const char*)(k + (size_t)tt * kBKV * ldk);
+    const char* vb = (const char*)(v + (size_t)tt * kBKV * ldv);
+    const unsigned dk = lds_base + (unsigned)(slot * kTileChunks + wave * kBlk * 64) * 16u;
+    const unsigned dv = dk + (unsigned)(kNBuf * kTileChunks) * 16u;
+    if (tt == last_tile) {
+#pragma unroll
+      for (int b = 0; b < kBlk; ++b) {
+        dma(voff_kl[b], kb, dk + b * 1024u);
+        dma(voff_vl[b], vb, dv + b * 1024u);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < kBlk; ++b) {
+        dma(voff_k[b], kb, dk + b * 1024u);
+        dma(voff_v[b], vb, dv + b * 1024u);
+      }
     }
   };
   constexpr int kLoadsPerTile = 2 * kBlk;  // per wave
@@ -162,50 +196,50 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
   // 16 j + 4 h + {0..3} (+ 8), h = lane / 32.
   // The key rows read are tr_key + 16 j (+ 8); adding 16 j or 8 keeps
   // row & 3, so the swizzled address of every read is the j = 0 address of
-  // its head-dim block plus a constant.
+  // its head-dim block in slot 0 plus a constant (the slot's offset and
+  // 2048 bytes per 8 keys), which goes into the instruction's offset field.
   const int g16 = lane >> 4, i16 = lane & 15;
   const int tr_key = 4 * lh + (i16 >> 2);
   const int tr_dim = 16 * (g16 & 1) + 4 * (i16 & 3);  // + 32 db
-  int tr_off[4];                                        // bf16 element offsets, j = 0
+  unsigned tr_addr[4];                                 // LDS byte addresses, slot 0, j = 0
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     const int dim = 32 * db + tr_dim;
-    tr_off[db] = v_phys(tr_key, dim >> 3) * 8 + (dim & 7);
+    tr_addr[db] = lds_base + (unsigned)(kNBuf * kTileChunks) * 16u +
+                  2u * (unsigned)(v_phys(tr_key, dim >> 3) * 8 + (dim & 7));
   }
   // The 16 transpose reads of a tile (4 head-dim blocks x 2 key groups x two
   // 8-key halves) are issued as one batch and waited for inside the same asm
   // block.  Through the builtin, the compiler would wait for every tile load
   // in flight before the first of them; the explicit waits and barriers below
   // already order them after the tile's data landed.
-  auto pv = [&](int slot, const bf16x8 (&pf)[2]) {
-    const unsigned base = (unsigned)(size_t)(lds_void_t*)vs_lds[slot];  // LDS byte address
-    unsigned addr[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) addr[db] = base + 2u * (unsigned)tr_off[db];
+  auto pv = [&](auto SLOT, const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+    constexpr int o0 = decltype(SLOT)::value * kTileChunks * 16;
     short4_t r[4][4];  // [db][j * 2 + half]
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %16\n\t"
-        "ds_read_b64_tr_b16 %1, %16 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %2, %16 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %3, %16 offset:6144\n\t"
-        "ds_read_b64_tr_b16 %4, %17\n\t"
-        "ds_read_b64_tr_b16 %5, %17 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %6, %17 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %7, %17 offset:6144\n\t"
-        "ds_read_b64_tr_b16 %8, %18\n\t"
-        "ds_read_b64_tr_b16 %9, %18 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %10, %18 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %11, %18 offset:6144\n\t"
-        "ds_read_b64_tr_b16 %12, %19\n\t"
-        "ds_read_b64_tr_b16 %13, %19 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %14, %19 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %15, %19 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %2, %16 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %3, %16 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %4, %17 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %6, %17 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %7, %17 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %8, %18 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %9, %18 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %11, %18 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %12, %19 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %13, %19 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %14, %19 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]),
           "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(r[1][2]), "=&v"(r[1][3]),
           "=&v"(r[2][0]), "=&v"(r[2][1]), "=&v"(r[2][2]), "=&v"(r[2][3]),
           "=&v"(r[3][0]), "=&v"(r[3][1]), "=&v"(r[3][2]), "=&v"(r[3][3])
-        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3])
+        : "v"(tr_addr[0]), "v"(tr_addr[1]), "v"(tr_addr[2]), "v"(tr_addr[3]),
+          "i"(o0), "i"(o0 + 2048), "i"(o0 + 4096), "i"(o0 + 6144)
         : "memory");
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -250,8 +284,11 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
 
   const int ntiles = (n + kBKV - 1) / kBKV;
   // Prologue: tiles 0..4 in flight, wait for 0, 1 and 2, scores of tile 0.
-#pragma unroll
-  for (int t = 0; t < kNBuf; ++t) issue_tile(t, t);
+  issue_tile(0, std::integral_constant<int, 0>{});
+  issue_tile(1, std::integral_constant<int, 1>{});
+  issue_tile(2, std::integral_constant<int, 2>{});
+  issue_tile(3, std::integral_constant<int, 3>{});
+  issue_tile(4, std::integral_constant<int, 4>{});
   wait_vmcnt<(kNBuf - 3) * kLoadsPerTile>();
   __syncthreads();
   floatx16 sa, sb;
@@ -259,18 +296,20 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
   scores(0, sa);
 
   // One step: scores of tile t+1 into `nxt` while the softmax of tile t (in
-  // `cur`) runs, then P V of tile t.  Steps come in pairs (the score buffers
-  // swap roles); a pair starts with tiles t .. t+2 landed for every wave, and
-  // the ring is refilled once per pair, at its end, with the two tiles whose
-  // slots the pair freed: a tile load is then never followed by an LDS read
-  // in the same loop iteration (the compiler would otherwise wait for every
-  // load in flight before that read).  Every step is unconditional: a tile
-  // index past the end reloads the last tile, and a step on such a tile masks
-  // all of its keys, so it adds nothing; an odd tile count runs one fully
-  // masked step.
-  auto step = [&](int t, floatx16& cur, floatx16& nxt) {
+  // `cur`) runs, then P V of tile t.  Tile t sits in ring slot t % 5; the
+  // loop below is unrolled over the ring's cycle (five pairs of steps), so
+  // every slot is a compile-time constant and each LDS address is a
+  // loop-invariant register plus an immediate offset.  Steps come in pairs
+  // (the score buffers swap roles); a pair starts with tiles t .. t+2 landed
+  // for every wave, and the ring is refilled once per pair, at its end, with
+  // the two tiles whose slots the pair freed.  Every step is unconditional: a
+  // tile index past the end reloads the last tile, and a step on such a tile
+  // masks all of its keys, so it adds nothing; an odd tile count runs one
+  // fully masked step.
+  auto step = [&](int t, auto CS, floatx16& cur, floatx16& nxt) __attribute__((always_inline)) {
+    constexpr int cs = decltype(CS)::value;
+    constexpr int ns = (cs + 1) % kNBuf;
     // K fragments of tile t+1, read ahead of the softmax's branches.
-    const int ns = (t + 1) % kNBuf;
     bf16x8 kf[8];
 #pragma unroll
     for (int st = 0; st < 8; ++st) kf[st] = ks_lds[ns][k_phys(lr, 2 * st + lh)];
@@ -290,17 +329,31 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
       }
     }
     l_run += psum;
-    pv(t % kNBuf, pf);
+    pv(CS, pf);
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, sa, sb);
-    step(t + 1, sb, sa);
+  auto pair = [&](int t, auto S0) __attribute__((always_inline)) {
+    constexpr int s0 = decltype(S0)::value;
+    constexpr int s1 = (s0 + 1) % kNBuf;
+    step(t, std::integral_constant<int, s0>{}, sa, sb);
+    step(t + 1, std::integral_constant<int, s1>{}, sb, sa);
     // Tiles t+3 and t+4 landed; every wave is done with the slots of tiles t
     // and t+1, which take tiles t+5 and t+6.
     wait_vmcnt<0>();
     __syncthreads();
-    issue_tile(t + kNBuf, t % kNBuf);
-    issue_tile(t + 1 + kNBuf, (t + 1) % kNBuf);
+    issue_tile(t + kNBuf, std::integral_constant<int, s0>{});
+    issue_tile(t + 1 + kNBuf, std::integral_constant<int, s1>{});
+  };
+  for (int t = 0;;) {
+    pair(t, std::integral_constant<int, 0>{});
+    if ((t += 2) >= ntiles) break;
+    pair(t, std::integral_constant<int, 2>{});
+    if ((t += 2) >= ntiles) break;
+    pair(t, std::integral_constant<int, 4>{});
+    if ((t += 2) >= ntiles) break;
+    pair(t, std::integral_constant<int, 1>{});
+    if ((t += 2) >= ntiles) break;
+    pair(t, std::integral_constant<int, 3>{});
+    if ((t += 2) >= ntiles) break;
   }
   wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
 
