@@ -81,6 +81,21 @@ int split_count(int m, int n, int k) {
 
 size_t split_bytes(int m, int n, int s) { return (size_t)s * ((m + 255) / 256) * 256 * n * 4; }
 
+// Skinny products (M <= 128): the weight-streaming kernel, split over K when
+// its slabs alone (N / 128 workgroups) leave most CUs idle and the caller lent
+// scratch (gated residual and fp32 products).
+bool skinny_shape(int m, int n, int k) { return m > 0 && m <= 128 && n % 128 == 0 && k % 64 == 0; }
+
+int skinny_split(int n, int k) {
+  const int slabs = n / 128, kt = k / 64;
+  int best = 1;
+  for (int d = 2; d <= 16 && kt / d >= 4; ++d)
+    if (kt % d == 0 && (long)slabs * d <= cu_count()) best = d;
+  return best;
+}
+
+size_t skinny_split_bytes(int m, int n, int d) { return (size_t)d * ((m + 31) / 32) * 32 * n * 4; }
+
 // Sum of the K-range partials, four columns per thread: gated (mod != null)
 // x[r][c] += gate[seg(r)][c] * sum_s part[s][r][c], else x[r][c] = sum.
 __global__ __launch_bounds__(256) void split_reduce_kernel(float* x, int ldx, const float* part,
@@ -180,8 +195,58 @@ void launch_gemm_fp8(const GemmArgs& g, hipStream_t st) {
 
 size_t gemm_split_ws_bytes(int m, int n, int k) {
   const int s = split_count(m, n, k);
-  return s > 1 ? split_bytes(m, n, s) : 0;
+  const size_t ring = s > 1 ? split_bytes(m, n, s) : 0;
+  if (!skinny_shape(m, n, k)) return ring;
+  const int d = skinny_split(n, k);
+  return std::max(ring, d > 1 ? skinny_split_bytes(m, n, d) : (size_t)0);
 }
+
+namespace {
+
+template <int MT, GemmEpi EPI>
+void launch_skinny(const GemmArgs& g, int ksplit, hipStream_t st) {
+  const int slabs = g.N / 128;
+  hipLaunchKernelGGL((gemm::gemm_skinny_kernel<MT, EPI>), dim3(slabs * ksplit), dim3(256), 0, st, g,
+                     slabs, g.K / 64 / ksplit);
+}
+
+template <int MT>
+void run_skinny_mt(const GemmArgs& g, hipStream_t st) {
+  const bool gated = g.epi == GemmEpi::kGatedResidual;
+  if ((gated || g.epi == GemmEpi::kStoreF32) && g.split_ws != nullptr) {
+    const int d = skinny_split(g.N, g.K);
+    if (d > 1 && skinny_split_bytes(g.M, g.N, d) <= g.split_ws_bytes) {
+      GemmArgs h = g;
+      h.epi = GemmEpi::kSplitPartial;
+      h.C = g.split_ws;
+      h.ldc = g.N;
+      launch_skinny<MT, GemmEpi::kSplitPartial>(h, d, st);
+      const size_t quads = (size_t)g.M * (g.N / 4);
+      hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st,
+                         (float*)g.C, g.ldc, (const float*)g.split_ws, (size_t)32 * MT * g.N, d, g.M,
+                         g.N, gated ? g.mod : nullptr, g.mod_stride, g.gate_offset, g.seg);
+      return;
+    }
+  }
+  switch (g.epi) {
+    case GemmEpi::kStoreBf16: launch_skinny<MT, GemmEpi::kStoreBf16>(g, 1, st); break;
+    case GemmEpi::kStoreF32: launch_skinny<MT, GemmEpi::kStoreF32>(g, 1, st); break;
+    case GemmEpi::kInProj: launch_skinny<MT, GemmEpi::kInProj>(g, 1, st); break;
+    case GemmEpi::kGatedResidual: launch_skinny<MT, GemmEpi::kGatedResidual>(g, 1, st); break;
+    case GemmEpi::kSplitPartial: break;
+  }
+}
+
+void run_skinny(const GemmArgs& g, hipStream_t st) {
+  switch ((g.M + 31) / 32) {
+    case 1: run_skinny_mt<1>(g, st); break;
+    case 2: run_skinny_mt<2>(g, st); break;
+    case 3: run_skinny_mt<3>(g, st); break;
+    default: run_skinny_mt<4>(g, st); break;
+  }
+}
+
+}  // namespace
 
 // Tile choice: 256x256 tiles on the persistent ring kernel (4 waves, 128x128
 // per wave) when there are at least 192 of them; otherwise the register-staged
@@ -190,6 +255,10 @@ size_t gemm_split_ws_bytes(int m, int n, int k) {
 // K % 64 == 0 and N % 64 == 0.
 void launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (g.M <= 0) return;
+  if (skinny_shape(g.M, g.N, g.K)) {
+    run_skinny(g, st);
+    return;
+  }
   const long big_tiles = (long)((g.M + 255) / 256) * (g.N / 256);
   // Gated residual and fp32 products with too few tiles to fill the chip and
   // a long K (the text stream's and small batches' output projection, the text

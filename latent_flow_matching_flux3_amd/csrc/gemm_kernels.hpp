@@ -670,5 +670,139 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
 }
 
+
+// ---------------------------------------------------------------------------
+// Skinny products (M <= 128 rows, e.g. the blocks of a 96-token image):
+// there is little MFMA work per weight byte, so the kernel is built to stream
+// the weight panel once at full memory rate rather than to fill 256x256
+// tiles (which would do up to 8x the MFMA work on padding rows).
+//
+// One workgroup per 128 output columns (a slab) and per K range; its rows are
+// all of M, padded to MT fragments of 32.  Four waves: wave (wn, wk) owns
+// output columns wn*64 .. wn*64+63 (two fragments, so each SwiGLU a/b pair of
+// the packed in-projection stays in one wave) and the k steps of parity wk of
+// every slice; the two K halves are added through LDS before the epilogue.
+// 64-wide K slices of X (MT*32 rows, rows past M-1 clamped) and W (128 rows)
+// go straight to LDS through a ring of four slots, three slices in flight
+// (direct-to-LDS loads as inline assembly, as in the ring kernel; the waits
+// and barriers below order them against the fragment reads).
+// ---------------------------------------------------------------------------
+template <int MT>
+struct SkinnyTile {
+  static constexpr int FM = MT, FN = 2;
+};
+
+template <int MT, GemmEpi EPI>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g, int slabs, int kt_per) {
+  using T = SkinnyTile<MT>;
+  using Lay = Layout<64>;
+  constexpr int CPR = Lay::CPR;            // 8 chunks of 16 bytes per row
+  constexpr int MP = 32 * MT;              // X rows in LDS
+  constexpr int BN = 128;                  // W rows (output columns) per slab
+  constexpr int STAGES = 4;
+  constexpr int STAGE = (MP + BN) * CPR;   // 16-byte chunks per slot
+  constexpr int X_BLK = MP / Lay::RPB;     // KiB blocks of X per slice
+  constexpr int BLK = X_BLK + BN / Lay::RPB;
+  static_assert(BLK % 4 == 0, "a slice's blocks split evenly over the 4 waves");
+  constexpr int PER = BLK / 4;             // loads per wave per slice
+  static_assert((STAGES - 1) * PER < 64, "vmcnt range");
+  static_assert(2 * MT * 2 * 16 * 64 * 4 <= STAGES * STAGE * 16, "K-half reduction fits the ring");
+  __shared__ bf16x8 lds[STAGES * STAGE];
+
+  const int slab = blockIdx.x % slabs, split = blockIdx.x / slabs;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 1, wk = wave >> 1;
+  const int n0 = slab * BN;
+  const size_t k0 = (size_t)split * kt_per * 64;
+
+  // Block b of a slice: X rows 8b .. 8b+7 (b < X_BLK), else W rows; lane t
+  // lands at row t/8, physical chunk t%8 of the block, so it fetches the
+  // logical chunk that maps there.  Wave w issues blocks w*PER .. w*PER+PER-1.
+  const char* xsrc = (const char*)(g.A + k0);
+  const char* wsrc = (const char*)(g.B + (size_t)n0 * g.ldb + k0);
+  const int sub_row = lane / CPR;
+  unsigned voff[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int b = wave * PER + q;
+    const int row = (b < X_BLK ? b : b - X_BLK) * Lay::RPB + sub_row;
+    const int chunk = (lane % CPR) ^ Lay::swz(row);
+    voff[q] = b < X_BLK ? (unsigned)((min(row, g.M - 1) * g.lda + chunk * 8) * 2)
+                        : (unsigned)((row * g.ldb + chunk * 8) * 2);
+  }
+  const unsigned lds_base = (unsigned)(size_t)(lds_void_t*)lds;
+  // Slice kt into slot `slot`; past the last slice the last one is loaded
+  // again (into a slot no longer read), so every iteration has the same
+  // number of loads in flight behind the slice it waits for.
+  auto issue_slice = [&](int kt, int slot) __attribute__((always_inline)) {
+    const int kc = min(kt, kt_per - 1) * 128;  // bytes
+    const unsigned dst = lds_base + (unsigned)(slot * STAGE) * 16u;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int b = wave * PER + q;
+      const char* src = (b < X_BLK ? xsrc : wsrc) + kc;
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :: "v"(voff[q]), "s"(src), "s"(dst + (unsigned)b * 1024u) : "m0");
+    }
+  };
+
+  floatx16 acc[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s + 1 < STAGES; ++s) issue_slice(s, s);
+  const int lr = lane & 31, lh = lane >> 5;
+  const int sw = Lay::swz(lr);  // fragment rows are 32 f + lr
+  for (int kt = 0; kt < kt_per; ++kt) {
+    wait_vmcnt<(STAGES - 2) * PER>();  // slice kt landed
+    __syncthreads();                   // ... for every wave; slice kt-1's slot is free
+    issue_slice(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    const int buf = (kt % STAGES) * STAGE;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ch = (2 * (2 * h + wk) + lh) ^ sw;
+      bf16x8 xf[MT], wf[2];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) xf[i] = lds[buf + (32 * i + lr) * CPR + ch];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) wf[j] = lds[buf + (MP + wn * 64 + 32 * j + lr) * CPR + ch];
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mma(xf[i], wf[j], acc[i][j]);
+    }
+  }
+  wait_vmcnt<0>();  // the trailing reloads may still be writing the ring
+  __syncthreads();
+
+  // Add the odd-k half into the even-k waves, which run the epilogue.
+  float* red = (float*)lds + (size_t)wn * (MT * 2 * 16 * 64);
+  if (wk == 1) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((i * 2 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+  }
+  __syncthreads();
+  if (wk == 0) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * 2 + j) * 16 + r) * 64 + lane];
+    const int wrow0 = EPI == GemmEpi::kSplitPartial ? split * MP : 0;
+    epilogue<T, EPI>(g, acc, wrow0, n0 + wn * 64);
+  }
+}
+
 }  // namespace gemm
 }  // namespace flux3

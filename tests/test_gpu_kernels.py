@@ -43,7 +43,8 @@ def test_ids_bit_exact_and_rope_table(L, lay):
 # ---- GEMMs -------------------------------------------------------------------------
 
 @pytest.mark.parametrize("m,n,k", [(1, 64, 64), (37, 128, 192), (300, 256, 320), (130, 3072, 128),
-                                   (1030, 13312, 128), (513, 27648, 64), (96, 3072, 12288)])
+                                   (1030, 13312, 128), (513, 27648, 64), (96, 3072, 12288),
+                                   (128, 27648, 3072), (65, 384, 4096)])
 def test_linear(L, m, n, k):
     x = syn.normal_bf16((m, k), 1.0, 11, f"lin.x.{m}.{k}")
     w = syn.normal_bf16((n, k), 0.02, 12, f"lin.w.{n}.{k}")
