@@ -307,6 +307,10 @@ size_t flux3_stack_workspace_size(int n_img, int n_cond, int n_txt);
  *           flux3_build_ids (same token order)
  *   sigma, sigma_next : the step's noise level and the one it jumps to
  *   v     : device output [n_img][128] fp32
+ * Stage 1's streams after the image one (references, text) run on a second
+ * HIP stream that the library keeps per device, forked from `stream` and
+ * joined back to it before stage 2 (so the call stays ordered on `stream`);
+ * while `stream` is being captured into a graph, everything runs on `stream`.
  */
 int flux3_stack_forward(const flux3_model_weights* w, const uint16_t* img, int n_img,
                         const uint16_t* cond, int n_cond, const uint16_t* txt, int n_txt,
@@ -324,9 +328,10 @@ int flux3_euler_step(float* x, uint16_t* x_bf16, const float* v, int n, float si
  * "Sampling"; [blog] "The denoising loop"): for k = 0..steps-1,
  *   v = flux3_stack_forward(bf16(x), sigmas[k], sigmas[k+1]);
  *   x <- x + (sigmas[k+1] - sigmas[k]) v.
- * Everything is enqueued on `stream` with no host synchronisation and no
- * allocation, so the call can be captured into one HIP graph by the caller
- * (the sigmas are read on the host at call time and baked into the launches).
+ * Everything is enqueued on `stream` (stage 1 as in flux3_stack_forward) with
+ * no host synchronisation and no allocation, so the call can be captured into
+ * one HIP graph by the caller (the sigmas are read on the host at call time
+ * and baked into the launches).
  *   x      : device [n_img][128] fp32 latents, in/out (the final x on return)
  *   cond, txt, table : as for flux3_stack_forward, constant over the loop
  *   sigmas : host [steps+1] fp32 (e.g. from flux3_sigmas), all finite
@@ -358,7 +363,9 @@ int flux3_build_ids_cfg(int img_h, int img_w, int n_refs, const int* ref_hw, int
  * reference streams go through stage 1 once (they are the same for both
  * samples); the texts run side by side, each attending to itself; stage 2 runs
  * both samples in one pass, each attending within itself; the final layer
- * gives v0 and v1, and v = v0 + guidance (v1 - v0).
+ * gives v0 and v1, and v = v0 + guidance (v1 - v0).  The reference and text
+ * streams' stage 1 runs on the library's side stream as in
+ * flux3_stack_forward.
  *   w        : model weights; ref_time_in NULL for the base checkpoint (if
  *              given, ref_time_in(emb(sigma_next)) is added as in the flow map)
  *   img      : device [n_img][128] bf16;  cond: device [n_cond][128] or NULL

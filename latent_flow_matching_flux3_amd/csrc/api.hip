@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/flux3_dit.h"
 #include "common.hpp"
@@ -563,12 +564,72 @@ struct StackWs {
   char* time_ws;    // kTimeWsBytes
   void* block_ws;   // block workspace for N rows
   size_t block_ws_bytes;
+  void* side_ws;    // block workspace of the stage-1 side stream (largest non-image stream)
 };
 
-size_t stack_ws_bytes(int n_total) {
+// Stage 1 runs each stream on its own rows with its own blocks, so the
+// non-image streams (references, text) do not depend on the image stream
+// until stage 2: they run on a second HIP stream beside it and fill CUs the
+// image stream's kernels leave idle (at 4096 image rows the output projection
+// has 192 tiles for 256 CUs, and the attention's second round of workgroups
+// is half full).  One side stream and one pair of fork / join events per
+// device, created on first use.  Each event record and the wait on it happen
+// under one lock: another caller recording the fork event in between would
+// let this call's side work start before its inputs are ready.  Not used
+// while the caller's stream is being captured into a graph (work another
+// thread queued on a forked side stream would land in that graph); stage 1
+// then runs on the caller's stream alone.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+// The current device's side stream, made to wait for everything queued on
+// `main` so far; null when there is none to use (capture, HIP failure).
+const SideStream* side_fork(hipStream_t main) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(main, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream& sd = g_side[dev];
+  if (sd.s == nullptr) {
+    SideStream x;
+    if (hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&x.join, hipEventDisableTiming) != hipSuccess) {
+      if (x.fork) (void)hipEventDestroy(x.fork);
+      (void)hipStreamDestroy(x.s);
+      return nullptr;
+    }
+    sd = x;
+  }
+  if (hipEventRecord(sd.fork, main) != hipSuccess || hipStreamWaitEvent(sd.s, sd.fork, 0) != hipSuccess)
+    return nullptr;
+  return &sd;
+}
+
+// `main` waits for everything queued on the side stream so far.
+int side_join(const SideStream* sd, hipStream_t main) {
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  const hipError_t e = hipEventRecord(sd->join, sd->s);
+  REQUIRE(e == hipSuccess, FLUX3_EHIP, "stage-1 join record: %s", hipGetErrorString(e));
+  const hipError_t f = hipStreamWaitEvent(main, sd->join, 0);
+  REQUIRE(f == hipSuccess, FLUX3_EHIP, "stage-1 join wait: %s", hipGetErrorString(f));
+  return FLUX3_OK;
+}
+
+// Rows of the largest stream that stage 1 may run beside the image stream.
+int side_rows(int n_cond, int n_txt) { return std::max(n_cond, n_txt); }
+
+size_t stack_ws_bytes(int n_img, int n_cond, int n_txt) {
+  const int n_total = n_img + n_cond + n_txt;
+  const int side = side_rows(n_cond, n_txt);
   return align256((size_t)n_total * kHidden * 4) + align256(3 * kHidden * 4) +
          2 * align256(3 * 3 * kHidden * 4) + align256(2 * kHidden * 4) + align256(kTimeWsBytes) +
-         block_ws_bytes(n_total);
+         block_ws_bytes(n_total) + (side > 0 ? block_ws_bytes(side) : 0);
 }
 
 StackWs carve_stack_ws(void* ws, int n_total) {
@@ -588,6 +649,7 @@ StackWs carve_stack_ws(void* ws, int n_total) {
   p += align256(kTimeWsBytes);
   s.block_ws = p;
   s.block_ws_bytes = block_ws_bytes(n_total);
+  s.side_ws = p + s.block_ws_bytes;
   return s;
 }
 }  // namespace
@@ -616,7 +678,7 @@ int flux3_time_vectors(const uint16_t* w_time_in, const uint16_t* w_time_out,
 size_t flux3_stack_workspace_size(int n_img, int n_cond, int n_txt) {
   const long n = (long)n_img + n_cond + n_txt;
   if (n_img <= 0 || n_cond < 0 || n_txt < 0 || n >= (1L << 30)) return 0;
-  return stack_ws_bytes((int)n);
+  return stack_ws_bytes(n_img, n_cond, n_txt);
 }
 
 }  // extern "C"
@@ -739,9 +801,13 @@ int stack_forward_unchecked(const flux3_model_weights* w, const uint16_t* img, i
     launch_gemm(g, stream);
   }
 
-  // a10: stage 1, each stream on its own rows with its own blocks.
+  // a10: stage 1, each stream on its own rows with its own blocks; the
+  // streams after the image one on the side stream when there is one.
+  const SideStream* side = n_modes > 1 ? side_fork(stream) : nullptr;
+  const BlockWs sws = side ? carve_block_ws(s.side_ws, side_rows(n_cond, n_txt)) : bws;
   for (int i = 0; i < n_modes; ++i) {
     const int m = modes[i];
+    const bool beside = side != nullptr && i > 0;
     SegTable seg{};
     seg.off[0] = 0;
     seg.off[1] = counts[i];
@@ -749,7 +815,12 @@ int stack_forward_unchecked(const flux3_model_weights* w, const uint16_t* img, i
     for (int b = 0; b < w->n_early; ++b)
       block_forward_unchecked(s.x + (size_t)row0[i] * kHidden, counts[i], seg,
                               s.mod_early + (size_t)i * 3 * kHidden, &w->early[m][b],
-                              table + (size_t)row0[i] * 128, bws, stream);
+                              table + (size_t)row0[i] * 128, beside ? sws : bws,
+                              beside ? side->s : stream);
+  }
+  if (side != nullptr) {
+    rc = side_join(side, stream);
+    if (rc) return rc;
   }
 
   // a11: stage 2, all tokens, per-row modulation by stream.
@@ -782,8 +853,8 @@ int stack_forward_unchecked(const flux3_model_weights* w, const uint16_t* img, i
 
 // flux3_sample's workspace: the stack's, then v [n_img][128] fp32 and the
 // bf16 copy of x [n_img][128] the embedding reads.
-size_t sample_ws_bytes(int n_img, int n_total) {
-  return stack_ws_bytes(n_total) + align256((size_t)n_img * 128 * 4) +
+size_t sample_ws_bytes(int n_img, int n_cond, int n_txt) {
+  return stack_ws_bytes(n_img, n_cond, n_txt) + align256((size_t)n_img * 128 * 4) +
          align256((size_t)n_img * 128 * 2);
 }
 }  // namespace
@@ -796,9 +867,8 @@ int flux3_stack_forward(const flux3_model_weights* w, const uint16_t* img, int n
                         void* workspace, size_t ws_bytes, hipStream_t stream) {
   int rc = check_stack_args(w, img, n_img, cond, n_cond, txt, n_txt, table, v, workspace);
   if (rc) return rc;
-  const int n_total = n_img + n_cond + n_txt;
-  REQUIRE(ws_bytes >= stack_ws_bytes(n_total), FLUX3_EWORKSPACE, "workspace %zu < %zu bytes",
-          ws_bytes, stack_ws_bytes(n_total));
+  REQUIRE(ws_bytes >= stack_ws_bytes(n_img, n_cond, n_txt), FLUX3_EWORKSPACE,
+          "workspace %zu < %zu bytes", ws_bytes, stack_ws_bytes(n_img, n_cond, n_txt));
   return stack_forward_unchecked(w, img, n_img, cond, n_cond, txt, n_txt, table, sigma,
                                  sigma_next, v, workspace, stream);
 }
@@ -806,7 +876,7 @@ int flux3_stack_forward(const flux3_model_weights* w, const uint16_t* img, int n
 size_t flux3_sample_workspace_size(int n_img, int n_cond, int n_txt) {
   const long n = (long)n_img + n_cond + n_txt;
   if (n_img <= 0 || n_cond < 0 || n_txt < 0 || n >= (1L << 30)) return 0;
-  return sample_ws_bytes(n_img, (int)n);
+  return sample_ws_bytes(n_img, n_cond, n_txt);
 }
 
 int flux3_sample(const flux3_model_weights* w, float* x, int n_img, const uint16_t* cond,
@@ -823,11 +893,10 @@ int flux3_sample(const flux3_model_weights* w, float* x, int n_img, const uint16
   int rc = check_stack_args(w, (const uint16_t*)x, n_img, cond, n_cond, txt, n_txt, table, x,
                             workspace);
   if (rc) return rc;
-  const int n_total = n_img + n_cond + n_txt;
-  REQUIRE(ws_bytes >= sample_ws_bytes(n_img, n_total), FLUX3_EWORKSPACE,
-          "workspace %zu < %zu bytes", ws_bytes, sample_ws_bytes(n_img, n_total));
+  REQUIRE(ws_bytes >= sample_ws_bytes(n_img, n_cond, n_txt), FLUX3_EWORKSPACE,
+          "workspace %zu < %zu bytes", ws_bytes, sample_ws_bytes(n_img, n_cond, n_txt));
   if (steps == 0) return FLUX3_OK;
-  char* p = (char*)workspace + stack_ws_bytes(n_total);
+  char* p = (char*)workspace + stack_ws_bytes(n_img, n_cond, n_txt);
   float* v = (float*)p;
   bf16* xb = (bf16*)(p + align256((size_t)n_img * 128 * 4));
   const int n_lat = n_img * 128;
@@ -892,12 +961,15 @@ struct CfgWs {
   char* time_ws;
   float* v_pair;     // [2][n_img][128]
   void* block_ws;
+  void* side_ws;     // block workspace of the stage-1 side stream
 };
 
 size_t cfg_ws_bytes(const CfgRows& r) {
   return align256((size_t)r.n() * kHidden * 4) + align256(3 * kHidden * 4) +
          align256(3 * 3 * kHidden * 4) + align256(5 * 3 * kHidden * 4) + align256(2 * kHidden * 4) +
-         align256(kTimeWsBytes) + align256((size_t)2 * r.n_img * 128 * 4) + block_ws_bytes(r.n());
+         align256(kTimeWsBytes) + align256((size_t)2 * r.n_img * 128 * 4) + block_ws_bytes(r.n()) +
+         (side_rows(r.n_cond, r.n_t0 + r.n_t1) > 0 ? block_ws_bytes(side_rows(r.n_cond, r.n_t0 + r.n_t1))
+                                                    : 0);
 }
 
 CfgWs carve_cfg_ws(void* ws, const CfgRows& r) {
@@ -918,6 +990,7 @@ CfgWs carve_cfg_ws(void* ws, const CfgRows& r) {
   s.v_pair = (float*)p;
   p += align256((size_t)2 * r.n_img * 128 * 4);
   s.block_ws = p;
+  s.side_ws = p + block_ws_bytes(r.n());
   return s;
 }
 
@@ -1018,7 +1091,12 @@ int stack_cfg_unchecked(const flux3_model_weights* w, const uint16_t* img, const
 
   // a10: stage 1.  Image and references once (sample 0's rows), then both
   // texts in one call with one attention group each; then sample 1 gets a
-  // copy of the shared streams.
+  // copy of the shared streams.  References and texts run on the side stream
+  // when there is one.
+  const int nt = r.n_t0 + r.n_t1;
+  const SideStream* side = (r.n_cond > 0 || nt > 0) ? side_fork(stream) : nullptr;
+  const BlockWs sws = side ? carve_block_ws(s.side_ws, side_rows(r.n_cond, nt)) : bws;
+  hipStream_t s1 = side ? side->s : stream;
   SegTable one{};
   one.n = 1;
   int mi = 0;
@@ -1033,10 +1111,9 @@ int stack_cfg_unchecked(const flux3_model_weights* w, const uint16_t* img, const
     for (int b = 0; b < w->n_early; ++b)
       block_forward_unchecked(s.x + (size_t)r.n_img * kHidden, r.n_cond, one,
                               s.mod_early + (size_t)mi * 3 * kHidden, &w->early[1][b],
-                              table + (size_t)r.n_img * 128, bws, stream);
+                              table + (size_t)r.n_img * 128, sws, s1);
     ++mi;
   }
-  const int nt = r.n_t0 + r.n_t1;
   if (nt > 0) {
     one.off[1] = nt;
     SegTable groups{};
@@ -1047,7 +1124,11 @@ int stack_cfg_unchecked(const flux3_model_weights* w, const uint16_t* img, const
     for (int b = 0; b < w->n_early; ++b)
       block_forward_unchecked(s.x + (size_t)r.txt0() * kHidden, nt, one,
                               s.mod_early + (size_t)mi * 3 * kHidden, &w->early[2][b],
-                              table + (size_t)r.txt0() * 128, bws, stream, &groups);
+                              table + (size_t)r.txt0() * 128, sws, s1, &groups);
+  }
+  if (side != nullptr) {
+    rc = side_join(side, stream);
+    if (rc) return rc;
   }
   {
     const hipError_t e = hipMemcpyAsync(s.x + (size_t)r.img1() * kHidden, s.x,
