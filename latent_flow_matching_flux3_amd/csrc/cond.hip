@@ -31,9 +31,12 @@ void launch_timestep_embedding(const Timesteps& ts, int nt, float* out, hipStrea
 // f = SiLU or identity.  W bf16 [rows][K] (K % 8 == 0, K <= 4096), x fp32.
 // Each wave keeps its slice of f(x) in registers and streams kGemvRows rows of
 // W (16-byte loads, 64 lanes across K), one wave reduction per row.
-constexpr int kGemvRowsPerWave = 4;
 constexpr int kGemvMaxChunksPerLane = 8;  // K <= 64 * 8 * 8 = 4096
 
+// RPW rows per wave, in groups of 4 whose weight loads are issued together.
+// Every workgroup first forms (SiLU of) x in registers; with more rows per
+// wave that preamble is spread over more weight bytes.
+template <int RPW>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvBatch batch, int rows, int K, int silu_x,
                                                    int accumulate) {
   const int b = blockIdx.y;
@@ -57,33 +60,42 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvBatch batch, int rows, in
       xv[i][e] = val;
     }
   }
-  const int r0 = (blockIdx.x * 4 + wave) * kGemvRowsPerWave;
+  const int r0 = (blockIdx.x * 4 + wave) * RPW;
+#pragma unroll 1
+  for (int g = 0; g < RPW; g += 4) {
 #pragma unroll
-  for (int rr = 0; rr < kGemvRowsPerWave; ++rr) {
-    const int r = r0 + rr;
-    if (r >= rows) break;
-    const bf16* wr = W + (size_t)r * K;
-    float acc = 0.f;
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = r0 + g + rr;
+      if (r >= rows) break;
+      const bf16* wr = W + (size_t)r * K;
+      float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < kGemvMaxChunksPerLane; ++i) {
-      const int c = lane + 64 * i;
-      if (c < nchunk) {
-        bf16x8 w8 = *(const bf16x8*)(wr + c * 8);
+      for (int i = 0; i < kGemvMaxChunksPerLane; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nchunk) {
+          bf16x8 w8 = *(const bf16x8*)(wr + c * 8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc += (float)w8[e] * xv[i][e];
+          for (int e = 0; e < 8; ++e) acc += (float)w8[e] * xv[i][e];
+        }
       }
+      acc = wave_sum(acc);
+      if (lane == 0) y[r] = accumulate ? y[r] + acc : acc;
     }
-    acc = wave_sum(acc);
-    if (lane == 0) y[r] = accumulate ? y[r] + acc : acc;
   }
 }
 
 void launch_gemv(const GemvBatch& batch, int nb, int rows, int K, bool silu_x, bool accumulate,
                  hipStream_t st) {
-  const int rows_per_block = 4 * kGemvRowsPerWave;
-  dim3 grid((rows + rows_per_block - 1) / rows_per_block, nb);
-  hipLaunchKernelGGL(gemv_kernel, grid, dim3(256), 0, st, batch, rows, K, silu_x ? 1 : 0,
-                     accumulate ? 1 : 0);
+  // 64 rows per workgroup once that still gives a few workgroups per CU.
+  if ((long)rows * nb >= 64L * 512) {
+    dim3 grid((rows + 63) / 64, nb);
+    hipLaunchKernelGGL(gemv_kernel<16>, grid, dim3(256), 0, st, batch, rows, K, silu_x ? 1 : 0,
+                       accumulate ? 1 : 0);
+  } else {
+    dim3 grid((rows + 15) / 16, nb);
+    hipLaunchKernelGGL(gemv_kernel<4>, grid, dim3(256), 0, st, batch, rows, K, silu_x ? 1 : 0,
+                       accumulate ? 1 : 0);
+  }
 }
 
 // x += (sigma_next - sigma) * v; xb = bf16(x).  v == nullptr: x unchanged,
