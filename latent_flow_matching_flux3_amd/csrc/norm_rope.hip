@@ -30,8 +30,17 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const float* __restric
   const int row = blockIdx.x * kLnRowsPerBlock + (threadIdx.x >> 6);
   if (row >= n) return;
   const float* xr = x + (size_t)row * ldx;
+  // The row's shift and scale are loaded with x (they do not depend on it).
+  const float* shift = mod + (size_t)seg_of_row(seg, row) * mod_stride;
+  const float* scale = shift + kHidden;
+  float4 shv[12], scv[12];
   float v[12][4];
   float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    shv[i] = *(const float4*)(shift + (lane + 64 * i) * 4);
+    scv[i] = *(const float4*)(scale + (lane + 64 * i) * 4);
+  }
 #pragma unroll
   for (int i = 0; i < 12; ++i) {
     const float4 c = *(const float4*)(xr + (lane + 64 * i) * 4);
@@ -52,14 +61,11 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const float* __restric
     }
   const float var = wave_sum(q) * (1.0f / kHidden);
   const float rstd = 1.0f / sqrtf(var + 1e-6f);
-  const float* shift = mod + (size_t)seg_of_row(seg, row) * mod_stride;
-  const float* scale = shift + kHidden;
   bf16* orow = out + (size_t)row * ldo;
 #pragma unroll
   for (int i = 0; i < 12; ++i) {
     const int c0 = (lane + 64 * i) * 4;
-    const float4 sh = *(const float4*)(shift + c0);
-    const float4 sc = *(const float4*)(scale + c0);
+    const float4 sh = shv[i], sc = scv[i];
     bf16x4 o;
     o[0] = to_bf16((1.0f + sc.x) * ((v[i][0] - mu) * rstd) + sh.x);
     o[1] = to_bf16((1.0f + sc.y) * ((v[i][1] - mu) * rstd) + sh.y);
