@@ -236,6 +236,64 @@ def test_block_scale_minus_one_is_identity(L):
     np.testing.assert_array_equal(f64(got), f64(x))
 
 
+# ---- a4..a5, a12: the block's two projections through their own entry points -----------------
+# Row counts that take each GEMM path: at most 128 rows (the weight-streaming
+# kernel), up to a few hundred (register-staged tiles), 1030 (the persistent
+# ring kernel, ragged last tile row; checked on sampled columns).
+
+@pytest.mark.parametrize("m", [1, 33, 96, 128, 129, 300, 1030])
+def test_block_in_proj(L, m):
+    """q|k|v = xm [Wq; Wk; Wv]^T and h = silu(a) * b with a, b the two halves
+    of xm Win^T ([blog] "Inside one block": the projections and the SwiGLU
+    MLP all read the modulated row; [issue] "Structure")."""
+    w = syn.block_weights(71, "single_blocks.0")
+    blk = L.PackedBlock(upload(w))
+    xm = syn.normal_bf16((m, 3072), 1.0, 72, f"inproj.x.{m}")
+    qkv = torch.empty((m, 3 * 3072), dtype=torch.bfloat16, device="cuda")
+    h = torch.empty((m, 9216), dtype=torch.bfloat16, device="cuda")
+    say(f"block_in_proj m={m}")
+    L.flux3_block_in_proj(dev(xm), blk.w_in, qkv, h)
+    torch.cuda.synchronize()
+    wf = to_f64(w)
+    x = f64(xm)
+    if m > 300:  # sampled columns of each output
+        cq = np.sort(np.random.default_rng(7).choice(9216, 256, replace=False))
+        ch = np.sort(np.random.default_rng(8).choice(9216, 256, replace=False))
+    else:
+        cq = ch = np.arange(9216)
+    wqkv = np.concatenate([wf["q_proj"], wf["k_proj"], wf["v_proj"]])
+    assert_agree(f64(qkv)[:, cq], x @ wqkv[cq].T, f"in_proj q|k|v m={m}")
+    a = x @ wf["mlp_in"][:9216][ch].T
+    b = x @ wf["mlp_in"][9216:][ch].T
+    assert_agree(f64(h)[:, ch], O.silu(a) * b, f"in_proj h m={m}")
+
+
+@pytest.mark.parametrize("m", [1, 96, 128, 300, 1030])
+def test_block_out_proj(L, m):
+    """x += gate[seg(row)] (o Wo^T + h Wout^T), [o | h] one product with
+    K = 12288 ([blog] "Inside one block"; [issue] "Structure": the gated
+    residual), with two row segments of different gates."""
+    w = syn.block_weights(73, "single_blocks.0")
+    blk = L.PackedBlock(upload(w))
+    cat = syn.normal_bf16((m, 12288), 1.0, 74, f"outproj.cat.{m}")
+    x0 = syn.normal_f32((m, 3072), 1.0, 75, f"outproj.x.{m}")
+    mods = syn.normal_f32((2, 3, 3072), 0.5, 76, "outproj.mods")
+    segs = [0, m // 3, m] if m > 1 else [0, 1]
+    x = dev(x0)
+    say(f"block_out_proj m={m}")
+    L.flux3_block_out_proj(dev(cat), blk.w_out, x, segs, dev(mods))
+    torch.cuda.synchronize()
+    wf = to_f64(w)
+    c = f64(cat)
+    upd = c[:, :3072] @ wf["attn_out"].T + c[:, 3072:] @ wf["mlp_out"].T
+    gate = np.empty((m, 3072))
+    for si, (lo, hi) in enumerate(zip(segs[:-1], segs[1:])):
+        gate[lo:hi] = f64(mods)[si, 2]
+    ref = f64(x0) + gate * upd
+    # fp32 accumulation of exact bf16 products: only summation-order error
+    np.testing.assert_allclose(f64(x), ref, rtol=1e-4, atol=1e-4 * np.abs(gate * upd).max())
+
+
 # ---- conditioning -------------------------------------------------------------------------------
 
 def test_time_vectors(L):
