@@ -35,6 +35,24 @@ def test_quantize_rows_bit_exact(L, rows, cols):
     np.testing.assert_array_equal(s.cpu().numpy(), scale)
 
 
+def test_pack_block_fp8_bit_exact(L):
+    """flux3_pack_block_fp8 (through PackedBlock(fp8=True)): the codes and
+    row scales of the packed w_in and w_out equal the oracle's rowwise
+    quantization of the packed bf16 rows (sampled rows of both)."""
+    w = syn.block_weights(78, "single_blocks.0")
+    wd = {k: dev(v) for k, v in w.items()}
+    w_in, w_out = L.flux3_pack_block(wd)
+    blk = L.PackedBlock(wd, fp8=True)
+    torch.cuda.synchronize()
+    w_in8, s_in, w_out8, s_out = (t.cpu() for t in blk.fp8)
+    rng = np.random.default_rng(9)
+    for packed, codes8, scale8, name in [(w_in, w_in8, s_in, "w_in"), (w_out, w_out8, s_out, "w_out")]:
+        rows = np.sort(rng.choice(packed.shape[0], 48, replace=False))
+        codes, scale, _ = O.quantize_rows_fp8(packed[rows].float().cpu().numpy())
+        np.testing.assert_array_equal(codes8[rows].numpy(), codes, err_msg=name)
+        np.testing.assert_array_equal(scale8[rows].numpy(), scale, err_msg=name)
+
+
 @pytest.mark.parametrize("m,n,k", [(300, 512, 3072), (513, 256, 256), (64, 27648, 3072), (130, 3072, 12288),
                                    (600, 27648, 3072)])
 def test_linear_fp8(L, m, n, k):

@@ -241,6 +241,21 @@ def test_block_scale_minus_one_is_identity(L):
 # kernel), up to a few hundred (register-staged tiles), 1030 (the persistent
 # ring kernel, ragged last tile row; checked on sampled columns).
 
+def test_pack_block_layout(L):
+    """flux3_pack_block bit for bit: w_in rows q | k | v, then mlp_in with its
+    a (first 9216 rows) and b (last 9216) halves interleaved in groups of 32
+    rows; w_out = [attn_out | mlp_out] along the input dimension."""
+    w = syn.block_weights(77, "single_blocks.0")
+    w_in, w_out = L.flux3_pack_block(upload(w))
+    torch.cuda.synchronize()
+    wi, wo = w_in.cpu(), w_out.cpu()
+    assert torch.equal(wi[:9216], torch.cat([w["q_proj"], w["k_proj"], w["v_proj"]]))
+    a, b = w["mlp_in"][:9216], w["mlp_in"][9216:]
+    inter = torch.stack([a.reshape(288, 32, 3072), b.reshape(288, 32, 3072)], dim=1).reshape(18432, 3072)
+    assert torch.equal(wi[9216:], inter)
+    assert torch.equal(wo, torch.cat([w["attn_out"], w["mlp_out"]], dim=1))
+
+
 @pytest.mark.parametrize("m", [1, 33, 96, 128, 129, 300, 1030])
 def test_block_in_proj(L, m):
     """q|k|v = xm [Wq; Wk; Wv]^T and h = silu(a) * b with a, b the two halves
