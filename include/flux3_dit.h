@@ -139,6 +139,27 @@ int flux3_qk_norm_rope(uint16_t* q, int ldq, uint16_t* k, int ldk, int n, const 
 int flux3_attention(const uint16_t* q, int ldq, const uint16_t* k, int ldk, const uint16_t* v,
                     int ldv, uint16_t* o, int ldo, int n, hipStream_t stream);
 
+/* flux3_attention_ws: the same operation on a balanced schedule.  The work is
+ * 24 * ceil(n/128) items (head, 128-row query block) of ceil(n/32) key tiles
+ * each; flux3_attention runs one workgroup per item, two per CU (512 at a
+ * time), so an item count a little past a multiple of 512 leaves most CUs
+ * idle in the last round.  Here, for more than 512 items, no multiple of 512,
+ * and at most three whole rounds, 512 workgroups run the whole rounds and
+ * then share the leftover items' key tiles in equal runs (at least a quarter
+ * of an item each, so at most five parts an item); the workgroup that finishes
+ * an item's last part merges the other parts' partial softmax states (running
+ * max, sum and unnormalised output, fp32) from the workspace.
+ * flux3_block_forward attends this way inside its workspace.
+ *   workspace: device, >= flux3_attention_workspace_size(n) bytes (0: the plain
+ *              schedule, workspace may be NULL); no contents expected on entry
+ *              (its counters are cleared on the stream first).  Calls that
+ *              overlap on one workspace race.
+ */
+size_t flux3_attention_workspace_size(int n);
+int flux3_attention_ws(const uint16_t* q, int ldq, const uint16_t* k, int ldk, const uint16_t* v,
+                       int ldv, uint16_t* o, int ldo, int n, void* workspace, size_t ws_bytes,
+                       hipStream_t stream);
+
 /* ---- projections -------------------------------------------------------------
  * flux3_linear: Y = X W^T, fp32 accumulation, rounded to bf16 (or fp32 when
  * y_f32 is set, then y is ignored).

@@ -65,6 +65,8 @@ _SIGS = {
     "flux3_ln_modulate": (I, [P, I, P, I, I, P, I, P, I, P]),
     "flux3_qk_norm_rope": (I, [P, I, P, I, I, P, P, P, P]),
     "flux3_attention": (I, [P, I, P, I, P, I, P, I, I, P]),
+    "flux3_attention_workspace_size": (S, [I]),
+    "flux3_attention_ws": (I, [P, I, P, I, P, I, P, I, I, P, S, P]),
     "flux3_linear": (I, [P, I, P, I, P, I, P, I, I, I, P]),
     "flux3_pack_block": (I, [P, P, P, P, P, P, P, P, P]),
     "flux3_block_in_proj": (I, [P, I, P, P, P, I, P]),
@@ -194,6 +196,18 @@ def flux3_qk_norm_rope(q, k, q_scale, k_scale, table, stream=None):
 def flux3_attention(q, k, v, o, stream=None):
     _check(lib().flux3_attention(_ptr(q), _ld(q), _ptr(k), _ld(k), _ptr(v), _ld(v), _ptr(o), _ld(o),
                                  q.shape[0], _stream(stream)))
+    return o
+
+
+def flux3_attention_workspace_size(n: int) -> int:
+    return lib().flux3_attention_workspace_size(n)
+
+
+def flux3_attention_ws(q, k, v, o, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().flux3_attention_ws(_ptr(q), _ld(q), _ptr(k), _ld(k), _ptr(v), _ld(v), _ptr(o), _ld(o),
+                                    q.shape[0], _ptr(workspace) if workspace is not None else None,
+                                    ws_bytes, _stream(stream)))
     return o
 
 

@@ -74,6 +74,8 @@ struct BlockWs {
   uint8_t* cat8;
   float* scale_in;
   float* scale_out;
+  void* attn_split;  // split attention's partial states and counters (or null)
+  int attn_counters;
 };
 
 size_t qkv_region_bytes(int n) {
@@ -82,7 +84,7 @@ size_t qkv_region_bytes(int n) {
 
 size_t block_ws_bytes(int n) {
   return align256((size_t)n * kHidden * 2) + qkv_region_bytes(n) + align256((size_t)n * kWOutCols * 2) +
-         align256((size_t)n * kWOutCols) + 2 * align256((size_t)n * 4);
+         align256((size_t)n * kWOutCols) + 2 * align256((size_t)n * 4) + attn_split_ws_bytes(n);
 }
 
 BlockWs carve_block_ws(void* ws, int n) {
@@ -100,6 +102,9 @@ BlockWs carve_block_ws(void* ws, int n) {
   w.scale_in = (float*)p;
   p += align256((size_t)n * 4);
   w.scale_out = (float*)p;
+  p += align256((size_t)n * 4);
+  w.attn_split = attn_split_ws_bytes(n) ? p : nullptr;
+  w.attn_counters = attn_split_counter_count(n);
   return w;
 }
 
@@ -195,7 +200,7 @@ void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
   }
   // a6: RMSNorm + RoPE on q and k
   launch_qk_norm_rope(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, n, B(w->q_scale),
-                      B(w->k_scale), table, st);
+                      B(w->k_scale), table, st, attn_split_counters(ws.attn_split), ws.attn_counters);
   // a7: attention -> first 3072 columns of cat, per row group
   const int ng = attn ? attn->n : 1;
   for (int gi = 0; gi < ng; ++gi) {
@@ -203,7 +208,7 @@ void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
     if (r1 <= r0) continue;
     const bf16* q = ws.qkv + (size_t)r0 * 3 * kHidden;
     launch_attention(q, 3 * kHidden, q + kHidden, 3 * kHidden, q + 2 * kHidden, 3 * kHidden,
-                     ws.cat + (size_t)r0 * kWOutCols, kWOutCols, r1 - r0, st);
+                     ws.cat + (size_t)r0 * kWOutCols, kWOutCols, r1 - r0, st, ws.attn_split);
   }
   // a8: gated residual
   if (fp8) {
@@ -346,6 +351,31 @@ int flux3_attention(const uint16_t* q, int ldq, const uint16_t* k, int ldk, cons
   REQUIRE_LD(ldv, kHidden);
   REQUIRE_LD(ldo, kHidden);
   launch_attention(B(q), ldq, B(k), ldk, B(v), ldv, B(o), ldo, n, stream);
+  return check_launch("attention");
+}
+
+size_t flux3_attention_workspace_size(int n) { return n > 0 && attn_split_used(n) ? attn_split_ws_bytes(n) : 0; }
+
+int flux3_attention_ws(const uint16_t* q, int ldq, const uint16_t* k, int ldk, const uint16_t* v,
+                       int ldv, uint16_t* o, int ldo, int n, void* workspace, size_t ws_bytes,
+                       hipStream_t stream) {
+  REQUIRE(n >= 0, FLUX3_EINVAL, "n=%d", n);
+  if (n == 0) return FLUX3_OK;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(o);
+  REQUIRE_LD(ldq, kHidden);
+  REQUIRE_LD(ldk, kHidden);
+  REQUIRE_LD(ldv, kHidden);
+  REQUIRE_LD(ldo, kHidden);
+  const size_t need = flux3_attention_workspace_size(n);
+  REQUIRE(ws_bytes >= need, FLUX3_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (need) {
+    REQUIRE_PTR(workspace);
+    launch_zero_ints(attn_split_counters(workspace), attn_split_counter_count(n), stream);
+  }
+  launch_attention(B(q), ldq, B(k), ldk, B(v), ldv, B(o), ldo, n, stream, need ? workspace : nullptr);
   return check_launch("attention");
 }
 

@@ -31,9 +31,15 @@
 //     after the first tile.
 //   - Workgroups of the same head are placed on the same XCD (3 heads per
 //     XCD), so that head's K/V stay in that XCD's L2.
+//   - Balanced schedule (given a workspace, at 1-3 whole rounds of items plus
+//     a part round): the whole rounds as above, then the leftover items' key
+//     tiles in equal runs over all 512 workgroups; an item's parts are merged
+//     by the workgroup that finishes last (exact: the partial states carry
+//     their own reference max).
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace flux3 {
@@ -50,6 +56,7 @@ constexpr float kSlack = 8.0f;          // allowed lag of the softmax reference 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gmem_void_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short short4_t;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // LDS layouts (64 banks x 4 bytes).  Rows are keys, 256 bytes = 16 chunks of
 // 16 bytes.
@@ -85,10 +92,28 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Partial softmax state of one part of a split item: the 64 accumulator
+// registers as 16 groups of four (each group a 16-byte value per thread,
+// thread-contiguous), then the row's reference max and partial sum, one value
+// per thread.
+constexpr int kPartFloats = 64 * kBQ * 2 + 2 * kBQ * 2;
+
+// SPLIT = false: one workgroup per (head, 128-row query block) item, all keys.
+// SPLIT = true (items > gridDim.x = 512, not a multiple of it): `rounds` whole
+// rounds of items, item r * gridDim.x + slot in round r, then the leftover
+// items' key tiles, item-major, cut into runs of `units` tiles (>= a quarter
+// of an item, so an item has at most five parts); run j belongs to the slot at
+// position j % band of XCD band j / band, so neighbouring runs (parts of one
+// item, one head) share an XCD and its L2.  Each part writes its partial state
+// to `part`, and the workgroup that brings cnt[item] to the item's part count
+// merges the others' states into its own, stores the rows and resets the
+// counter.
+template <bool SPLIT>
 __global__ __launch_bounds__(kBQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict__ k, int ldk,
                      const bf16* __restrict__ v, int ldv, bf16* __restrict__ o, int ldo, int n,
-                     float scale_log2) {
+                     float scale_log2, float* __restrict__ part, int* __restrict__ cnt, int rounds,
+                     int units, int band) {
   // One LDS object for both rings: with several, the compiler gives each its
   // own alias scope and then waits for every tile load in flight before any
   // LDS read that may alias one (the explicit waits below are exact).
@@ -97,15 +122,49 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
   bf16x8 (*vs_lds)[kTileChunks] = (bf16x8 (*)[kTileChunks])(ring_lds + kNBuf * kTileChunks);
 
   const int nqb = (n + kBQ - 1) / kBQ;
-  const int total = nqb * kHeads;  // multiple of 8
-  const int lin = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int head = lin / nqb;
-  const int qb = lin % nqb;
+  const int ntiles = (n + kBKV - 1) / kBKV;
+  // Virtual slot: consecutive slots share an XCD (workgroup b runs on XCD b % 8).
+  const int band_len = gridDim.x >> 3;
+  const int vslot = (blockIdx.x & 7) * band_len + (blockIdx.x >> 3);
+  int r = 0;               // whole rounds done
+  int run = 0, u = 0, u_end = 0;  // the leftover run: units [u, u_end)
+  if constexpr (SPLIT) {
+    const int pos = vslot % band_len;
+    run = (vslot / band_len) * band + pos;
+    if (pos < band) {
+      u = run * units;
+      u_end = min(u + units, (nqb * kHeads - rounds * (int)gridDim.x) * ntiles);
+    }
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lh = lane >> 5;
+  const int sub_row = lane >> 4, pchunk = lane & 15;
+  const unsigned lds_base = (unsigned)(size_t)(lds_void_t*)ring_lds;
+
+  for (;;) {
+  int item, k_lo, k_hi;  // this part: key tiles [k_lo, k_hi) of item
+  if (!SPLIT) {
+    item = vslot;
+    k_lo = 0;
+    k_hi = ntiles;
+  } else if (r < rounds) {
+    item = r++ * (int)gridDim.x + vslot;
+    k_lo = 0;
+    k_hi = ntiles;
+  } else {
+    if (u >= u_end) return;
+    const int it = u / ntiles;
+    item = rounds * (int)gridDim.x + it;
+    k_lo = u - it * ntiles;
+    k_hi = min(ntiles, k_lo + (u_end - u));
+    u += k_hi - k_lo;
+  }
+  const int kend = min(n, k_hi * kBKV);           // keys at or past kend are masked
+  const int head = item / nqb;
+  const int qb = item - head * nqb;
   const int hoff = head * kHeadDim;
 
   // Q^T fragments of this wave's 32 rows, in registers for the whole kernel:
@@ -127,7 +186,6 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
   // state, load; no register results): the explicit waits and barriers below
   // order them against the LDS reads, and the compiler then adds no waits of
   // its own.
-  const int sub_row = lane >> 4, pchunk = lane & 15;
   constexpr int kBlk = kBKV / 4 / kWaves;  // KiB blocks of K (and of V) per wave per tile
   const int last_tile = (n - 1) / kBKV;
   const int last_rows = n - last_tile * kBKV;  // keys in the last tile (1 .. 32)
@@ -143,14 +201,13 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
     voff_kl[b] = (unsigned)((rl * ldk + hoff + kc * 8) * 2);
     voff_vl[b] = (unsigned)((rl * ldv + hoff + vc * 8) * 2);
   }
-  const unsigned lds_base = (unsigned)(size_t)(lds_void_t*)ring_lds;
   auto dma = [&](unsigned voff, const void* base, unsigned dst) __attribute__((always_inline)) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"(base), "s"(dst) : "m0");
   };
   auto issue_tile = [&](int tile, auto SLOT) __attribute__((always_inline)) {
     constexpr int slot = decltype(SLOT)::value;
-    const int tt = min(tile, last_tile);  // a tile past the end reloads the last one
+    const int tt = min(tile, k_hi - 1);  // a tile past the part's end reloads its last one
     const char* kb = (const char*)(k + (size_t)tt * kBKV * ldk);
     const char* vb = (const char*)(v + (size_t)tt * kBKV * ldv);
     const unsigned dk = lds_base + (unsigned)(slot * kTileChunks + wave * kBlk * 64) * 16u;
@@ -255,11 +312,11 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
   // (rare) move of the reference max with the rescale of O and l.  Both tests
   // are wave-uniform branches, kept ahead of the branch-free part below.
   auto softmax_head = [&](floatx16& s, int key0) {
-    if (key0 + kBKV > n) {  // keys past the end get probability 0
+    if (key0 + kBKV > kend) {  // keys past the part's end get probability 0
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (key >= n) s[r] = -INFINITY;
+        if (key >= kend) s[r] = -INFINITY;
       }
     }
     float mx = s[0];
@@ -282,13 +339,13 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
     }
   };
 
-  const int ntiles = (n + kBKV - 1) / kBKV;
-  // Prologue: tiles 0..4 in flight, wait for 0, 1 and 2, scores of tile 0.
-  issue_tile(0, std::integral_constant<int, 0>{});
-  issue_tile(1, std::integral_constant<int, 1>{});
-  issue_tile(2, std::integral_constant<int, 2>{});
-  issue_tile(3, std::integral_constant<int, 3>{});
-  issue_tile(4, std::integral_constant<int, 4>{});
+  // Prologue: tiles k_lo .. k_lo+4 in flight, wait for the first three,
+  // scores of the first.  Tile t sits in ring slot (t - k_lo) % 5.
+  issue_tile(k_lo, std::integral_constant<int, 0>{});
+  issue_tile(k_lo + 1, std::integral_constant<int, 1>{});
+  issue_tile(k_lo + 2, std::integral_constant<int, 2>{});
+  issue_tile(k_lo + 3, std::integral_constant<int, 3>{});
+  issue_tile(k_lo + 4, std::integral_constant<int, 4>{});
   wait_vmcnt<(kNBuf - 3) * kLoadsPerTile>();
   __syncthreads();
   floatx16 sa, sb;
@@ -343,19 +400,83 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
     issue_tile(t + kNBuf, std::integral_constant<int, s0>{});
     issue_tile(t + 1 + kNBuf, std::integral_constant<int, s1>{});
   };
-  for (int t = 0;;) {
+  for (int t = k_lo;;) {
     pair(t, std::integral_constant<int, 0>{});
-    if ((t += 2) >= ntiles) break;
+    if ((t += 2) >= k_hi) break;
     pair(t, std::integral_constant<int, 2>{});
-    if ((t += 2) >= ntiles) break;
+    if ((t += 2) >= k_hi) break;
     pair(t, std::integral_constant<int, 4>{});
-    if ((t += 2) >= ntiles) break;
+    if ((t += 2) >= k_hi) break;
     pair(t, std::integral_constant<int, 1>{});
-    if ((t += 2) >= ntiles) break;
+    if ((t += 2) >= k_hi) break;
     pair(t, std::integral_constant<int, 3>{});
-    if ((t += 2) >= ntiles) break;
+    if ((t += 2) >= k_hi) break;
   }
-  wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
+  // No load may still be writing LDS when the part (or the workgroup) ends.
+  wait_vmcnt<0>();
+
+  if (SPLIT && (k_lo > 0 || k_hi < ntiles)) {
+    // A part of a split item.  A run holds at most two partial parts: one
+    // starting inside an item (its first part, side 0) and one starting at
+    // an item's first tile (its last part, side 1).  The parts of an item are
+    // in runs first .. last: side 1 of run first, side 0 of the others.
+    const int side = k_lo > 0 ? 0 : 1;
+    // The workgroups of an item may run on different XCDs, whose L2s are not
+    // coherent with each other: the state goes out through stores that write
+    // through to memory and comes back through loads that bypass the
+    // non-coherent caches (system-coherent cache policy, SC1), so no fence
+    // has to write back or invalidate a whole L2 (which would also evict the
+    // K and V tiles other workgroups are streaming).  Every store is complete
+    // (vmcnt 0) before the barrier and the counter is bumped after it, so the
+    // workgroup that arrives last sees every state.
+    constexpr int kSC1 = 16;  // buffer cache-policy bit
+    const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
+        part + ((size_t)run * 2 + side) * kPartFloats, (short)0, kPartFloats * 4, 0x00020000);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const floatx16& a = oacc[c >> 2];
+      const int e = 4 * (c & 3);
+      const u32x4 d = {__float_as_uint(a[e]), __float_as_uint(a[e + 1]), __float_as_uint(a[e + 2]),
+                       __float_as_uint(a[e + 3])};
+      __builtin_amdgcn_raw_buffer_store_b128(d, mine, tid * 16, c * kBQ * 2 * 16, kSC1);
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run), mine, tid * 4, 64 * kBQ * 2 * 4, kSC1);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_run), mine, tid * 4, 65 * kBQ * 2 * 4, kSC1);
+    wait_vmcnt<0>();
+    __syncthreads();
+    int* flag = (int*)ring_lds;  // the count is passed on through the (drained) ring
+    if (tid == 0)
+      flag[0] = __hip_atomic_fetch_add(cnt + item, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int arrived = flag[0];
+    __syncthreads();  // every wave has read the flag before the ring is reused
+    const int t0 = (item - rounds * (int)gridDim.x) * ntiles;  // the item's first leftover unit
+    const int first = t0 / units, last = (t0 + ntiles - 1) / units;
+    if (arrived != last - first) continue;
+    // Last to arrive: merge the other parts' states.
+    for (int j = first; j <= last; ++j) {
+      if (j == run) continue;
+      const __amdgpu_buffer_rsrc_t other = __builtin_amdgcn_make_buffer_rsrc(
+          part + ((size_t)j * 2 + (j == first ? 1 : 0)) * kPartFloats, (short)0, kPartFloats * 4,
+          0x00020000);
+      const float m_o = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(other, tid * 4, 64 * kBQ * 2 * 4, kSC1));
+      const float l_o = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(other, tid * 4, 65 * kBQ * 2 * 4, kSC1));
+      const float m_new = fmaxf(m_run, m_o);
+      const float fa = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float fb = __builtin_amdgcn_exp2f(m_o - m_new);
+      m_run = m_new;
+      l_run = l_run * fa + l_o * fb;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(other, tid * 16, c * kBQ * 2 * 16, kSC1);
+        floatx16& a = oacc[c >> 2];
+        const int e0 = 4 * (c & 3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e0 + e] = a[e0 + e] * fa + __uint_as_float(t[e]) * fb;
+      }
+    }
+    if (tid == 0) __hip_atomic_store(cnt + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   // Normalise and store: lane holds query row lr, dims db*32 + 8 g + 4 lh + 0..3.
   const float inv = 1.0f / half_sum(l_run);
@@ -372,17 +493,89 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
         *(bf16x4*)(op + db * 32 + 8 * g4 + 4 * lh) = t;
       }
   }
+  if (!SPLIT) break;
+  }  // parts
 }
 
 }  // namespace
 
-void launch_attention(const bf16* q, int ldq, const bf16* k, int ldk, const bf16* v, int ldv,
-                      bf16* o, int ldo, int n, hipStream_t st) {
+namespace {
+
+// Two workgroups on each of the 256 CUs.
+constexpr int kSplitSlots = 512;
+
+int attn_items(int n) { return (n + kBQ - 1) / kBQ * kHeads; }
+
+struct SplitPlan {
+  int rounds = 0;  // whole rounds of items
+  int units = 0;   // key tiles per leftover run (0: no split)
+  int band = 0;    // leftover runs per XCD band
+};
+
+// The split schedule for n rows: none where the items fill whole rounds of
+// the slots, or less than one round, or where the leftover items would take
+// nearly a whole round anyway.  Nor past three whole rounds: the kernel runs
+// at its power limit, so a partly filled last round runs at a higher clock
+// and costs less than its share of the rounds, and after many rounds the
+// parts' extra loads and merges cost more than the idle slots (measured:
+// 2817 rows -16%, 4096 -9%, 4608 -2%, 8272 -8%, but 20992 rows, 7 whole
+// rounds, +1%).
+SplitPlan attn_split_plan(int n) {
+  SplitPlan p;
+  const int items = attn_items(n);
+  if (items <= kSplitSlots || items % kSplitSlots == 0 || items / kSplitSlots > 3) return p;
+  const long T = (n + kBKV - 1) / kBKV;
+  const long tail_units = (long)(items % kSplitSlots) * T;
+  const long units = std::max((tail_units + kSplitSlots - 1) / kSplitSlots, (T + 3) / 4);
+  if (units * 8 > T * 7) return p;
+  const long runs = (tail_units + units - 1) / units;
+  p.rounds = items / kSplitSlots;
+  p.units = (int)units;
+  p.band = (int)((runs + 7) / 8);
+  return p;
+}
+
+}  // namespace
+
+bool attn_split_used(int n) { return n > 0 && attn_split_plan(n).units > 0; }
+
+size_t attn_split_ws_bytes(int n) {
+  if (n <= 0 || attn_items(n) <= kSplitSlots) return 0;
+  return (size_t)kSplitSlots * 2 * kPartFloats * sizeof(float) +
+         ((size_t)attn_items(n) * sizeof(int) + 255) / 256 * 256;
+}
+
+int* attn_split_counters(void* ws) {
+  return ws ? (int*)((char*)ws + (size_t)kSplitSlots * 2 * kPartFloats * sizeof(float)) : nullptr;
+}
+
+int attn_split_counter_count(int n) { return attn_split_ws_bytes(n) ? attn_items(n) : 0; }
+
+namespace {
+__global__ void zero_ints_kernel(int* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+}  // namespace
+
+void launch_zero_ints(int* p, int n, hipStream_t st) {
   if (n <= 0) return;
-  const int nqb = (n + kBQ - 1) / kBQ;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
+}
+
+void launch_attention(const bf16* q, int ldq, const bf16* k, int ldk, const bf16* v, int ldv,
+                      bf16* o, int ldo, int n, hipStream_t st, void* split_ws) {
+  if (n <= 0) return;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHeadDim);
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(nqb * kHeads), dim3(kBQ * 2), 0, st, q, ldq, k, ldk, v, ldv,
-                     o, ldo, n, scale_log2);
+  const SplitPlan plan = split_ws ? attn_split_plan(n) : SplitPlan{};
+  if (plan.units > 0) {
+    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(kSplitSlots), dim3(kBQ * 2), 0, st, q, ldq, k, ldk,
+                       v, ldv, o, ldo, n, scale_log2, (float*)split_ws, attn_split_counters(split_ws),
+                       plan.rounds, plan.units, plan.band);
+    return;
+  }
+  hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(attn_items(n)), dim3(kBQ * 2), 0, st, q, ldq, k, ldk,
+                     v, ldv, o, ldo, n, scale_log2, nullptr, nullptr, 0, 0, 0);
 }
 
 }  // namespace flux3

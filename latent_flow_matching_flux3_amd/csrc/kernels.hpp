@@ -71,10 +71,23 @@ void launch_quant_rows_fp8(const bf16* x, int ldx, int rows, int cols, uint8_t* 
 void launch_ln_modulate(const float* x, int ldx, bf16* out, int ldo, int n, const SegTable& seg,
                         const float* mod, int mod_stride, hipStream_t st);
 void launch_rope_table(const float* ids, int n, float* table, hipStream_t st);
+// zero[0 .. nzero) is cleared on the way (the split attention's counters).
 void launch_qk_norm_rope(bf16* q, int ldq, bf16* k, int ldk, int n, const bf16* q_scale,
-                         const bf16* k_scale, const float* table, hipStream_t st);
+                         const bf16* k_scale, const float* table, hipStream_t st, int* zero = nullptr,
+                         int nzero = 0);
+// split_ws: attn_split_ws_bytes(n') bytes for some n' >= n, whose counters
+// (attn_split_counters) are zero; they are zero again when the launch ends.
+// With split_ws == nullptr (or a row count that fills whole rounds of
+// workgroups) every workgroup takes whole items.
 void launch_attention(const bf16* q, int ldq, const bf16* k, int ldk, const bf16* v, int ldv,
-                      bf16* o, int ldo, int n, hipStream_t st);
+                      bf16* o, int ldo, int n, hipStream_t st, void* split_ws = nullptr);
+// The balanced schedule is used for n (given a workspace); the workspace
+// (attn_split_ws_bytes) is sized for every row count up to n.
+bool attn_split_used(int n);
+size_t attn_split_ws_bytes(int n);
+int* attn_split_counters(void* ws);
+int attn_split_counter_count(int n);
+void launch_zero_ints(int* p, int n, hipStream_t st);
 void launch_gemm(const GemmArgs& a, hipStream_t st);
 struct Timesteps {
   float t[4];

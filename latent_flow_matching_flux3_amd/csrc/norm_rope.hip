@@ -113,9 +113,12 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(bf16* __restrict__ q,
                                                            bf16* __restrict__ k, int ldk, int n,
                                                            const bf16* __restrict__ q_scale,
                                                            const bf16* __restrict__ k_scale,
-                                                           const float* __restrict__ table) {
+                                                           const float* __restrict__ table,
+                                                           int* __restrict__ zero, int nzero) {
   const int tok = blockIdx.x;
   if (tok >= n) return;
+  if (tok == 0)
+    for (int i = threadIdx.x; i < nzero; i += 256) zero[i] = 0;
   const int lane16 = threadIdx.x & 15;
   const int vec_id = threadIdx.x >> 4;  // 0..15 head vectors per pass
   const int d0 = lane16 * 8;
@@ -157,10 +160,11 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(bf16* __restrict__ q,
 }
 
 void launch_qk_norm_rope(bf16* q, int ldq, bf16* k, int ldk, int n, const bf16* q_scale,
-                         const bf16* k_scale, const float* table, hipStream_t st) {
+                         const bf16* k_scale, const float* table, hipStream_t st, int* zero,
+                         int nzero) {
   if (n <= 0) return;
   hipLaunchKernelGGL(qk_norm_rope_kernel, dim3(n), dim3(256), 0, st, q, ldq, k, ldk, n, q_scale,
-                     k_scale, table);
+                     k_scale, table, zero, nzero);
 }
 
 }  // namespace flux3

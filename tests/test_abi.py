@@ -92,6 +92,12 @@ def test_error_codes(L):
     assert lib.flux3_block_forward(16, 10, segs, 1, 16, C.byref(w), 16, None, 1 << 30, None) == L.EWORKSPACE
     # empty inputs are a no-op
     assert lib.flux3_attention(None, 3072, None, 3072, None, 3072, None, 3072, 0, None) == L.OK
+    assert lib.flux3_attention_ws(None, 3072, None, 3072, None, 3072, None, 3072, 0, None, 0, None) == L.OK
+    # the balanced attention schedule needs its workspace where it applies (4608 rows: 864 items)
+    assert L.flux3_attention_workspace_size(4608) > 512 * 2 * 128 * 128 * 4
+    assert L.flux3_attention_workspace_size(2688) == 0 and L.flux3_attention_workspace_size(0) == 0
+    assert lib.flux3_attention_ws(16, 3072, 16, 3072, 16, 3072, 16, 3072, 4608, 16, 1000, None) == L.EWORKSPACE
+    assert lib.flux3_attention_ws(16, 3072, 16, 3072, 16, 3072, 16, 3072, 4608, None, 1 << 30, None) == L.EINVAL
     assert lib.flux3_block_forward(None, 0, None, 0, None, None, None, None, 0, None) == L.OK
     # workspace sizes grow with n and are 0 for n = 0
     assert L.flux3_block_workspace_size(0) == 0

@@ -184,6 +184,54 @@ def test_attention_special_cases(L):
     np.testing.assert_array_equal(f64(o1), f64(d1[:, 6144:]))
 
 
+@pytest.mark.parametrize("n", [2817, 4608, 8272])
+def test_attention_balanced_schedule(L, n):
+    """flux3_attention_ws: whole rounds of 512 (head, query block) items, then
+    the leftover items' key tiles shared out over the workgroups, the parts of
+    a cut item merged by the one that finishes last.  2817 rows: 552 items, 40
+    leftover in parts of 23 tiles (up to five parts an item; 23 query blocks,
+    a ragged one; 89 key tiles, the last one 1 key); 4608 rows: 352 leftover,
+    two or three parts; 8272 rows: three whole rounds, then 24 items in up to
+    five parts.  Two calls in a row on one workspace (its counters must come
+    back to zero), the second with other data; every row against the oracle
+    at 2817 rows, three rows of every query block (so every item, cut or not)
+    above."""
+    ws_bytes = L.flux3_attention_workspace_size(n)
+    assert ws_bytes > 0
+    ws = L.workspace(ws_bytes)
+    if n < 3000:
+        rows = np.arange(n)
+    else:
+        rows = np.array(sorted({min(b + r, n - 1) for b in range(0, n, 128) for r in (0, 77, 127)}))
+    for call in range(2):
+        qkv = syn.normal_bf16((n, 9216), 1.0 + call, 54 + call, f"att.ws.{n}.{call}")
+        d = dev(qkv)
+        o = torch.empty((n, 3072), dtype=torch.bfloat16, device="cuda")
+        say(f"attention_ws n={n} call={call}")
+        L.flux3_attention_ws(d[:, :3072], d[:, 3072:6144], d[:, 6144:], o, ws)
+        torch.cuda.synchronize()
+        q, k, v = (f64(qkv[:, i * 3072:(i + 1) * 3072]).reshape(n, 24, 128) for i in range(3))
+        ref = O.attention(q[rows], k, v).reshape(len(rows), 3072)
+        assert_agree(f64(o)[rows], ref, f"attention_ws n={n} call={call}")
+
+
+def test_attention_ws_plain_sizes(L):
+    """Item counts at or below one round of 512 workgroups, or a whole number
+    of rounds, need no workspace: flux3_attention_ws runs the plain schedule."""
+    assert L.flux3_attention_workspace_size(2688) == 0      # 21 blocks x 24 heads = 504 items
+    assert L.flux3_attention_workspace_size(65536) == 0     # 512 x 24 items: 24 whole rounds
+    assert L.flux3_attention_workspace_size(20992) == 0     # 3936 items: 7 whole rounds
+    assert L.flux3_attention_workspace_size(2689) > 0
+    n = 300
+    qkv = syn.normal_bf16((n, 9216), 1.0, 56, "att.ws.plain")
+    d = dev(qkv)
+    o = torch.empty((n, 3072), dtype=torch.bfloat16, device="cuda")
+    L.flux3_attention_ws(d[:, :3072], d[:, 3072:6144], d[:, 6144:], o, None)
+    torch.cuda.synchronize()
+    q, k, v = (f64(qkv[:, i * 3072:(i + 1) * 3072]).reshape(n, 24, 128) for i in range(3))
+    assert_agree(f64(o), O.attention(q, k, v).reshape(n, 3072), "attention_ws plain")
+
+
 # ---- a3..a8: one block ------------------------------------------------------------------------
 
 def _block_inputs(seed, lay, mod_scale=0.5):
