@@ -213,6 +213,13 @@ def test_attention_balanced_schedule(L, n):
         q, k, v = (f64(qkv[:, i * 3072:(i + 1) * 3072]).reshape(n, 24, 128) for i in range(3))
         ref = O.attention(q[rows], k, v).reshape(len(rows), 3072)
         assert_agree(f64(o)[rows], ref, f"attention_ws n={n} call={call}")
+        # The workspace ends with one int counter per item (256-byte aligned
+        # block); the workgroup that merges an item resets its counter, so a
+        # launch leaves them all zero: a block's later attention groups (the
+        # guided pack's two samples) start from zero without a clearing kernel.
+        items = 24 * ((n + 127) // 128)
+        cnt = ws[ws_bytes - (items * 4 + 255) // 256 * 256:][:items * 4].view(torch.int32)
+        assert int(cnt.abs().sum().item()) == 0, "split counters not reset"
 
 
 def test_attention_ws_plain_sizes(L):
