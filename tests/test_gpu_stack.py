@@ -90,6 +90,26 @@ def test_stack_reduced_depth(L, lay, n_early, n_single):
     assert_agree(f64(v), ref, f"stack n={lay.n_total}")
 
 
+@pytest.mark.timeout(600)
+def test_stack_full_tokens_reduced_depth(L):
+    """The benchmarked launch, flux3_stack_forward on the 1024^2 text-to-image
+    tokens (64x64 image + 512 text = 4608), at depth 1 + 1: stage 1 on its two
+    streams (the 4096-row image block on the balanced attention schedule, the
+    text block on the side stream), the joint block at 4608 rows (balanced
+    schedule too), the final layer; every output row against the oracle."""
+    lay = syn.WORKLOADS["stack_t2i_1024_4608tok"]
+    seed = 17
+    say(f"stack n={lay.n_total} depth 1+1")
+    wts = Weights(L, seed, lay, 1, 1)
+    img, cond, txt = _inputs(lay, seed)
+    sig, sig_next = np.float32(0.6), np.float32(0.45)
+    v = _gpu_stack(L, wts, lay, img, cond, txt, float(sig), float(sig_next))
+    say("  oracle")
+    ref = O.stack_forward(wts.W, wts.B, f64(img), None, f64(txt), lay.img_h, lay.img_w, [],
+                          float(sig), float(sig_next), 1, 1)
+    assert_agree(f64(v), ref, f"stack n={lay.n_total} depth 1+1")
+
+
 @pytest.mark.timeout(900)
 def test_stack_full_depth(L):
     """All 5 + 28 blocks and every checkpoint tensor, at the smallest
