@@ -96,6 +96,15 @@ def test_error_codes(L):
     # the balanced attention schedule needs its workspace where it applies (4608 rows: 864 items)
     assert L.flux3_attention_workspace_size(4608) > 512 * 2 * 128 * 128 * 4
     assert L.flux3_attention_workspace_size(2688) == 0 and L.flux3_attention_workspace_size(0) == 0
+    # where the balanced schedule applies: 24 * ceil(n/128) items, more than one round of 512, not
+    # a whole number of rounds, at most three whole rounds, leftover items short of 7/8 of a round
+    for n, used in [(2689, True), (4096, True), (4608, True), (8272, True), (8704, True),
+                    (5376, False),     # 1008 items: 496 leftover, nearly a whole round
+                    (10880, False),    # 2040 items: 3 rounds + 504 leftover
+                    (10752, False),    # 2016 items: 3 rounds + 480 leftover (> 7/8)
+                    (12288, False),    # 2304 items: 4 whole rounds + 256 (past three rounds)
+                    (20992, False), (49136, False), (65536, False)]:
+        assert (L.flux3_attention_workspace_size(n) > 0) == used, n
     assert lib.flux3_attention_ws(16, 3072, 16, 3072, 16, 3072, 16, 3072, 4608, 16, 1000, None) == L.EWORKSPACE
     assert lib.flux3_attention_ws(16, 3072, 16, 3072, 16, 3072, 16, 3072, 4608, None, 1 << 30, None) == L.EINVAL
     assert lib.flux3_block_forward(None, 0, None, 0, None, None, None, None, 0, None) == L.OK
