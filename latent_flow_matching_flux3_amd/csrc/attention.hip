@@ -145,355 +145,357 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
   const unsigned lds_base = (unsigned)(size_t)(lds_void_t*)ring_lds;
 
   for (;;) {
-  int item, k_lo, k_hi;  // this part: key tiles [k_lo, k_hi) of item
-  if (!SPLIT) {
-    item = vslot;
-    k_lo = 0;
-    k_hi = ntiles;
-  } else if (r < rounds) {
-    item = r++ * (int)gridDim.x + vslot;
-    k_lo = 0;
-    k_hi = ntiles;
-  } else {
-    if (u >= u_end) return;
-    const int it = u / ntiles;
-    item = rounds * (int)gridDim.x + it;
-    k_lo = u - it * ntiles;
-    k_hi = min(ntiles, k_lo + (u_end - u));
-    u += k_hi - k_lo;
-  }
-  const int kend = min(n, k_hi * kBKV);           // keys at or past kend are masked
-  const int head = item / nqb;
-  const int qb = item - head * nqb;
-  const int hoff = head * kHeadDim;
-
-  // Q^T fragments of this wave's 32 rows, in registers for the whole kernel:
-  // the B operand of k-step st is query row lr, dims 16 st + 8 lh .. +8.
-  bf16x8 qf[8];
-  {
-    const int grow = min(qb * kBQ + wave * 32 + lr, n - 1);
-    const bf16x8* qp = (const bf16x8*)(q + (size_t)grow * ldq + hoff);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) qf[st] = qp[2 * st + lh];
-  }
-
-  // Tile loads: each wave fills 2 KiB of K and 2 KiB of V per tile, 1 KiB
-  // (4 key rows) per global_load_lds_dwordx4; lane t lands at row t/16,
-  // physical chunk t%16 and so fetches the logical chunk that maps there.
-  // The source is a scalar base (the tile's first key row) plus a fixed
-  // 32-bit lane offset; a partial last tile uses lane offsets whose rows are
-  // clamped to the last key.  The loads are inline assembly (m0 set, one wait
-  // state, load; no register results): the explicit waits and barriers below
-  // order them against the LDS reads, and the compiler then adds no waits of
-  // its own.
-  constexpr int kBlk = kBKV / 4 / kWaves;  // KiB blocks of K (and of V) per wave per tile
-  const int last_tile = (n - 1) / kBKV;
-  const int last_rows = n - last_tile * kBKV;  // keys in the last tile (1 .. 32)
-  unsigned voff_k[kBlk], voff_v[kBlk], voff_kl[kBlk], voff_vl[kBlk];
-#pragma unroll
-  for (int b = 0; b < kBlk; ++b) {
-    const int row = (wave * kBlk + b) * 4 + sub_row;  // 0..31
-    const int rl = min(row, last_rows - 1);
-    const int kc = pchunk ^ (row & 15);
-    const int vc = pchunk ^ (4 * (row & 3));
-    voff_k[b] = (unsigned)((row * ldk + hoff + kc * 8) * 2);
-    voff_v[b] = (unsigned)((row * ldv + hoff + vc * 8) * 2);
-    voff_kl[b] = (unsigned)((rl * ldk + hoff + kc * 8) * 2);
-    voff_vl[b] = (unsigned)((rl * ldv + hoff + vc * 8) * 2);
-  }
-  auto dma = [&](unsigned voff, const void* base, unsigned dst) __attribute__((always_inline)) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(voff), "s"(base), "s"(dst) : "m0");
-  };
-  auto issue_tile = [&](int tile, auto SLOT) __attribute__((always_inline)) {
-    constexpr int slot = decltype(SLOT)::value;
-    const int tt = min(tile, k_hi - 1);  // a tile past the part's end reloads its last one
-    const char* kb = (const char*)(k + (size_t)tt * kBKV * ldk);
-    const char* vb = (const char*)(v + (size_t)tt * kBKV * ldv);
-    const unsigned dk = lds_base + (unsigned)(slot * kTileChunks + wave * kBlk * 64) * 16u;
-    const unsigned dv = dk + (unsigned)(kNBuf * kTileChunks) * 16u;
-    if (tt == last_tile) {
-#pragma unroll
-      for (int b = 0; b < kBlk; ++b) {
-        dma(voff_kl[b], kb, dk + b * 1024u);
-        dma(voff_vl[b], vb, dv + b * 1024u);
-      }
+    int item, k_lo, k_hi;  // this part: key tiles [k_lo, k_hi) of item
+    if (!SPLIT) {
+      item = vslot;
+      k_lo = 0;
+      k_hi = ntiles;
+    } else if (r < rounds) {
+      item = r++ * (int)gridDim.x + vslot;
+      k_lo = 0;
+      k_hi = ntiles;
     } else {
+      if (u >= u_end) return;
+      const int it = u / ntiles;
+      item = rounds * (int)gridDim.x + it;
+      k_lo = u - it * ntiles;
+      k_hi = min(ntiles, k_lo + (u_end - u));
+      u += k_hi - k_lo;
+    }
+    const int kend = min(n, k_hi * kBKV);           // keys at or past kend are masked
+    const int head = item / nqb;
+    const int qb = item - head * nqb;
+    const int hoff = head * kHeadDim;
+
+    // Q^T fragments of this wave's 32 rows, in registers for the whole kernel:
+    // the B operand of k-step st is query row lr, dims 16 st + 8 lh .. +8.
+    bf16x8 qf[8];
+    {
+      const int grow = min(qb * kBQ + wave * 32 + lr, n - 1);
+      const bf16x8* qp = (const bf16x8*)(q + (size_t)grow * ldq + hoff);
 #pragma unroll
-      for (int b = 0; b < kBlk; ++b) {
-        dma(voff_k[b], kb, dk + b * 1024u);
-        dma(voff_v[b], vb, dv + b * 1024u);
+      for (int st = 0; st < 8; ++st) qf[st] = qp[2 * st + lh];
+    }
+
+    // Tile loads: each wave fills 2 KiB of K and 2 KiB of V per tile, 1 KiB
+    // (4 key rows) per global_load_lds_dwordx4; lane t lands at row t/16,
+    // physical chunk t%16 and so fetches the logical chunk that maps there.
+    // The source is a scalar base (the tile's first key row) plus a fixed
+    // 32-bit lane offset; a partial last tile uses lane offsets whose rows are
+    // clamped to the last key.  The loads are inline assembly (m0 set, one wait
+    // state, load; no register results): the explicit waits and barriers below
+    // order them against the LDS reads, and the compiler then adds no waits of
+    // its own.
+    constexpr int kBlk = kBKV / 4 / kWaves;  // KiB blocks of K (and of V) per wave per tile
+    const int last_tile = (n - 1) / kBKV;
+    const int last_rows = n - last_tile * kBKV;  // keys in the last tile (1 .. 32)
+    unsigned voff_k[kBlk], voff_v[kBlk], voff_kl[kBlk], voff_vl[kBlk];
+#pragma unroll
+    for (int b = 0; b < kBlk; ++b) {
+      const int row = (wave * kBlk + b) * 4 + sub_row;  // 0..31
+      const int rl = min(row, last_rows - 1);
+      const int kc = pchunk ^ (row & 15);
+      const int vc = pchunk ^ (4 * (row & 3));
+      voff_k[b] = (unsigned)((row * ldk + hoff + kc * 8) * 2);
+      voff_v[b] = (unsigned)((row * ldv + hoff + vc * 8) * 2);
+      voff_kl[b] = (unsigned)((rl * ldk + hoff + kc * 8) * 2);
+      voff_vl[b] = (unsigned)((rl * ldv + hoff + vc * 8) * 2);
+    }
+    auto dma = [&](unsigned voff, const void* base, unsigned dst) __attribute__((always_inline)) {
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :: "v"(voff), "s"(base), "s"(dst) : "m0");
+    };
+    auto issue_tile = [&](int tile, auto SLOT) __attribute__((always_inline)) {
+      constexpr int slot = decltype(SLOT)::value;
+      const int tt = min(tile, k_hi - 1);  // a tile past the part's end reloads its last one
+      const char* kb = (const char*)(k + (size_t)tt * kBKV * ldk);
+      const char* vb = (const char*)(v + (size_t)tt * kBKV * ldv);
+      const unsigned dk = lds_base + (unsigned)(slot * kTileChunks + wave * kBlk * 64) * 16u;
+      const unsigned dv = dk + (unsigned)(kNBuf * kTileChunks) * 16u;
+      if (tt == last_tile) {
+#pragma unroll
+        for (int b = 0; b < kBlk; ++b) {
+          dma(voff_kl[b], kb, dk + b * 1024u);
+          dma(voff_vl[b], vb, dv + b * 1024u);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < kBlk; ++b) {
+          dma(voff_k[b], kb, dk + b * 1024u);
+          dma(voff_v[b], vb, dv + b * 1024u);
+        }
       }
-    }
-  };
-  constexpr int kLoadsPerTile = 2 * kBlk;  // per wave
+    };
+    constexpr int kLoadsPerTile = 2 * kBlk;  // per wave
 
-  // S^T = K Q^T for one tile (one 32-key fragment).
-  auto scores = [&](int slot, floatx16& s) {
-    const floatx16 zero = {};
+    // S^T = K Q^T for one tile (one 32-key fragment).
+    auto scores = [&](int slot, floatx16& s) {
+      const floatx16 zero = {};
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const bf16x8 a = ks_lds[slot][k_phys(lr, 2 * st + lh)];
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], st == 0 ? zero : s, 0, 0, 0);
-    }
-  };
-
-  floatx16 oacc[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
-  float m_run = -INFINITY;  // running max (scaled, base-2 domain) of row lr
-  float l_run = 0.f;        // this lane's partial row sum
-
-  // Transpose-read geometry: within its 16-lane group (g = lane / 16, i =
-  // lane % 16) a lane supplies the address of key 4h + i/4 (+ 16 j, + 8 for
-  // the second half of the fragment) and head dims 32 db + 16 (g % 2) +
-  // 4 (i % 4) .. +3; it receives head dim 32 db + lane % 32 of keys
-  // 16 j + 4 h + {0..3} (+ 8), h = lane / 32.
-  // The key rows read are tr_key + 16 j (+ 8); adding 16 j or 8 keeps
-  // row & 3, so the swizzled address of every read is the j = 0 address of
-  // its head-dim block in slot 0 plus a constant (the slot's offset and
-  // 2048 bytes per 8 keys), which goes into the instruction's offset field.
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const int tr_key = 4 * lh + (i16 >> 2);
-  const int tr_dim = 16 * (g16 & 1) + 4 * (i16 & 3);  // + 32 db
-  unsigned tr_addr[4];                                 // LDS byte addresses, slot 0, j = 0
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int dim = 32 * db + tr_dim;
-    tr_addr[db] = lds_base + (unsigned)(kNBuf * kTileChunks) * 16u +
-                  2u * (unsigned)(v_phys(tr_key, dim >> 3) * 8 + (dim & 7));
-  }
-  // The 16 transpose reads of a tile (4 head-dim blocks x 2 key groups x two
-  // 8-key halves) are issued as one batch and waited for inside the same asm
-  // block.  Through the builtin, the compiler would wait for every tile load
-  // in flight before the first of them; the explicit waits and barriers below
-  // already order them after the tile's data landed.
-  auto pv = [&](auto SLOT, const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
-    constexpr int o0 = decltype(SLOT)::value * kTileChunks * 16;
-    short4_t r[4][4];  // [db][j * 2 + half]
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %1, %16 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %2, %16 offset:%22\n\t"
-        "ds_read_b64_tr_b16 %3, %16 offset:%23\n\t"
-        "ds_read_b64_tr_b16 %4, %17 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %5, %17 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %6, %17 offset:%22\n\t"
-        "ds_read_b64_tr_b16 %7, %17 offset:%23\n\t"
-        "ds_read_b64_tr_b16 %8, %18 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %9, %18 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %10, %18 offset:%22\n\t"
-        "ds_read_b64_tr_b16 %11, %18 offset:%23\n\t"
-        "ds_read_b64_tr_b16 %12, %19 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %13, %19 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %14, %19 offset:%22\n\t"
-        "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]),
-          "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(r[1][2]), "=&v"(r[1][3]),
-          "=&v"(r[2][0]), "=&v"(r[2][1]), "=&v"(r[2][2]), "=&v"(r[2][3]),
-          "=&v"(r[3][0]), "=&v"(r[3][1]), "=&v"(r[3][2]), "=&v"(r[3][3])
-        : "v"(tr_addr[0]), "v"(tr_addr[1]), "v"(tr_addr[2]), "v"(tr_addr[3]),
-          "i"(o0), "i"(o0 + 2048), "i"(o0 + 4096), "i"(o0 + 6144)
-        : "memory");
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(r[db][2 * j], r[db][2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[j], oacc[db], 0, 0, 0);
+      for (int st = 0; st < 8; ++st) {
+        const bf16x8 a = ks_lds[slot][k_phys(lr, 2 * st + lh)];
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], st == 0 ? zero : s, 0, 0, 0);
       }
-  };
+    };
 
-  // Softmax of tile t, first part: mask keys past the end, row max, and the
-  // (rare) move of the reference max with the rescale of O and l.  Both tests
-  // are wave-uniform branches, kept ahead of the branch-free part below.
-  auto softmax_head = [&](floatx16& s, int key0) {
-    if (key0 + kBKV > kend) {  // keys past the part's end get probability 0
+    floatx16 oacc[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (key >= kend) s[r] = -INFINITY;
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
+    float m_run = -INFINITY;  // running max (scaled, base-2 domain) of row lr
+    float l_run = 0.f;        // this lane's partial row sum
+
+    // Transpose-read geometry: within its 16-lane group (g = lane / 16, i =
+    // lane % 16) a lane supplies the address of key 4h + i/4 (+ 16 j, + 8 for
+    // the second half of the fragment) and head dims 32 db + 16 (g % 2) +
+    // 4 (i % 4) .. +3; it receives head dim 32 db + lane % 32 of keys
+    // 16 j + 4 h + {0..3} (+ 8), h = lane / 32.
+    // The key rows read are tr_key + 16 j (+ 8); adding 16 j or 8 keeps
+    // row & 3, so the swizzled address of every read is the j = 0 address of
+    // its head-dim block in slot 0 plus a constant (the slot's offset and
+    // 2048 bytes per 8 keys), which goes into the instruction's offset field.
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int tr_key = 4 * lh + (i16 >> 2);
+    const int tr_dim = 16 * (g16 & 1) + 4 * (i16 & 3);  // + 32 db
+    unsigned tr_addr[4];                                 // LDS byte addresses, slot 0, j = 0
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int dim = 32 * db + tr_dim;
+      tr_addr[db] = lds_base + (unsigned)(kNBuf * kTileChunks) * 16u +
+                    2u * (unsigned)(v_phys(tr_key, dim >> 3) * 8 + (dim & 7));
+    }
+    // The 16 transpose reads of a tile (4 head-dim blocks x 2 key groups x two
+    // 8-key halves) are issued as one batch and waited for inside the same asm
+    // block.  Through the builtin, the compiler would wait for every tile load
+    // in flight before the first of them; the explicit waits and barriers below
+    // already order them after the tile's data landed.
+    auto pv = [&](auto SLOT, const bf16x8 (&pf)[2]) __attribute__((always_inline)) {
+      constexpr int o0 = decltype(SLOT)::value * kTileChunks * 16;
+      short4_t r[4][4];  // [db][j * 2 + half]
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"
+          "ds_read_b64_tr_b16 %1, %16 offset:%21\n\t"
+          "ds_read_b64_tr_b16 %2, %16 offset:%22\n\t"
+          "ds_read_b64_tr_b16 %3, %16 offset:%23\n\t"
+          "ds_read_b64_tr_b16 %4, %17 offset:%20\n\t"
+          "ds_read_b64_tr_b16 %5, %17 offset:%21\n\t"
+          "ds_read_b64_tr_b16 %6, %17 offset:%22\n\t"
+          "ds_read_b64_tr_b16 %7, %17 offset:%23\n\t"
+          "ds_read_b64_tr_b16 %8, %18 offset:%20\n\t"
+          "ds_read_b64_tr_b16 %9, %18 offset:%21\n\t"
+          "ds_read_b64_tr_b16 %10, %18 offset:%22\n\t"
+          "ds_read_b64_tr_b16 %11, %18 offset:%23\n\t"
+          "ds_read_b64_tr_b16 %12, %19 offset:%20\n\t"
+          "ds_read_b64_tr_b16 %13, %19 offset:%21\n\t"
+          "ds_read_b64_tr_b16 %14, %19 offset:%22\n\t"
+          "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]),
+            "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(r[1][2]), "=&v"(r[1][3]),
+            "=&v"(r[2][0]), "=&v"(r[2][1]), "=&v"(r[2][2]), "=&v"(r[2][3]),
+            "=&v"(r[3][0]), "=&v"(r[3][1]), "=&v"(r[3][2]), "=&v"(r[3][3])
+          : "v"(tr_addr[0]), "v"(tr_addr[1]), "v"(tr_addr[2]), "v"(tr_addr[3]),
+            "i"(o0), "i"(o0 + 2048), "i"(o0 + 4096), "i"(o0 + 6144)
+          : "memory");
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(r[db][2 * j], r[db][2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[j], oacc[db], 0, 0, 0);
+        }
+    };
+
+    // Softmax of tile t, first part: mask keys past the end, row max, and the
+    // (rare) move of the reference max with the rescale of O and l.  Both tests
+    // are wave-uniform branches, kept ahead of the branch-free part below.
+    auto softmax_head = [&](floatx16& s, int key0) {
+      if (key0 + kBKV > kend) {  // keys past the part's end get probability 0
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          if (key >= kend) s[r] = -INFINITY;
+        }
       }
-    }
-    float mx = s[0];
+      float mx = s[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = half_max(mx) * scale_log2;
-    // The reference max may lag the true running max by up to kSlack (base 2),
-    // so probabilities stay <= 2^kSlack; O and l share the reference, so the
-    // result is unchanged while the rescale (a wave-wide 64-register update)
-    // is only needed when some row's max jumps by more than that.
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = half_max(mx) * scale_log2;
+      // The reference max may lag the true running max by up to kSlack (base 2),
+      // so probabilities stay <= 2^kSlack; O and l share the reference, so the
+      // result is unchanged while the rescale (a wave-wide 64-register update)
+      // is only needed when some row's max jumps by more than that.
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-    }
-  };
-
-  // Prologue: tiles k_lo .. k_lo+4 in flight, wait for the first three,
-  // scores of the first.  Tile t sits in ring slot (t - k_lo) % 5.
-  issue_tile(k_lo, std::integral_constant<int, 0>{});
-  issue_tile(k_lo + 1, std::integral_constant<int, 1>{});
-  issue_tile(k_lo + 2, std::integral_constant<int, 2>{});
-  issue_tile(k_lo + 3, std::integral_constant<int, 3>{});
-  issue_tile(k_lo + 4, std::integral_constant<int, 4>{});
-  wait_vmcnt<(kNBuf - 3) * kLoadsPerTile>();
-  __syncthreads();
-  floatx16 sa, sb;
-  bf16x8 pf[2];
-  scores(0, sa);
-
-  // One step: scores of tile t+1 into `nxt` while the softmax of tile t (in
-  // `cur`) runs, then P V of tile t.  Tile t sits in ring slot t % 5; the
-  // loop below is unrolled over the ring's cycle (five pairs of steps), so
-  // every slot is a compile-time constant and each LDS address is a
-  // loop-invariant register plus an immediate offset.  Steps come in pairs
-  // (the score buffers swap roles); a pair starts with tiles t .. t+2 landed
-  // for every wave, and the ring is refilled once per pair, at its end, with
-  // the two tiles whose slots the pair freed.  Every step is unconditional: a
-  // tile index past the end reloads the last tile, and a step on such a tile
-  // masks all of its keys, so it adds nothing; an odd tile count runs one
-  // fully masked step.
-  auto step = [&](int t, auto CS, floatx16& cur, floatx16& nxt) __attribute__((always_inline)) {
-    constexpr int cs = decltype(CS)::value;
-    constexpr int ns = (cs + 1) % kNBuf;
-    // K fragments of tile t+1, read ahead of the softmax's branches.
-    bf16x8 kf[8];
-#pragma unroll
-    for (int st = 0; st < 8; ++st) kf[st] = ks_lds[ns][k_phys(lr, 2 * st + lh)];
-    softmax_head(cur, t * kBKV);
-    // One branch-free region: the score MFMAs of tile t+1 with the
-    // exponentials of tile t between them (two per MFMA).
-    const floatx16 zero = {};
-    float psum = 0.f;
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], st == 0 ? zero : nxt, 0, 0, 0);
-#pragma unroll
-      for (int r = 2 * st; r < 2 * st + 2; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(cur[r], scale_log2, -m_run));
-        psum += p;
-        pf[r >> 3][r & 7] = to_bf16(p);
+          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
       }
+    };
+
+    // Prologue: tiles k_lo .. k_lo+4 in flight, wait for the first three,
+    // scores of the first.  Tile t sits in ring slot (t - k_lo) % 5.
+    issue_tile(k_lo, std::integral_constant<int, 0>{});
+    issue_tile(k_lo + 1, std::integral_constant<int, 1>{});
+    issue_tile(k_lo + 2, std::integral_constant<int, 2>{});
+    issue_tile(k_lo + 3, std::integral_constant<int, 3>{});
+    issue_tile(k_lo + 4, std::integral_constant<int, 4>{});
+    wait_vmcnt<(kNBuf - 3) * kLoadsPerTile>();
+    __syncthreads();
+    floatx16 sa, sb;
+    bf16x8 pf[2];
+    scores(0, sa);
+
+    // One step: scores of tile t+1 into `nxt` while the softmax of tile t (in
+    // `cur`) runs, then P V of tile t.  Tile t sits in ring slot t % 5; the
+    // loop below is unrolled over the ring's cycle (five pairs of steps), so
+    // every slot is a compile-time constant and each LDS address is a
+    // loop-invariant register plus an immediate offset.  Steps come in pairs
+    // (the score buffers swap roles); a pair starts with tiles t .. t+2 landed
+    // for every wave, and the ring is refilled once per pair, at its end, with
+    // the two tiles whose slots the pair freed.  Every step is unconditional: a
+    // tile index past the end reloads the last tile, and a step on such a tile
+    // masks all of its keys, so it adds nothing; an odd tile count runs one
+    // fully masked step.
+    auto step = [&](int t, auto CS, floatx16& cur, floatx16& nxt) __attribute__((always_inline)) {
+      constexpr int cs = decltype(CS)::value;
+      constexpr int ns = (cs + 1) % kNBuf;
+      // K fragments of tile t+1, read ahead of the softmax's branches.
+      bf16x8 kf[8];
+#pragma unroll
+      for (int st = 0; st < 8; ++st) kf[st] = ks_lds[ns][k_phys(lr, 2 * st + lh)];
+      softmax_head(cur, t * kBKV);
+      // One branch-free region: the score MFMAs of tile t+1 with the
+      // exponentials of tile t between them (two per MFMA).
+      const floatx16 zero = {};
+      float psum = 0.f;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], st == 0 ? zero : nxt, 0, 0, 0);
+#pragma unroll
+        for (int r = 2 * st; r < 2 * st + 2; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(cur[r], scale_log2, -m_run));
+          psum += p;
+          pf[r >> 3][r & 7] = to_bf16(p);
+        }
+      }
+      l_run += psum;
+      pv(CS, pf);
+    };
+    auto pair = [&](int t, auto S0) __attribute__((always_inline)) {
+      constexpr int s0 = decltype(S0)::value;
+      constexpr int s1 = (s0 + 1) % kNBuf;
+      step(t, std::integral_constant<int, s0>{}, sa, sb);
+      step(t + 1, std::integral_constant<int, s1>{}, sb, sa);
+      // Tiles t+3 and t+4 landed; every wave is done with the slots of tiles t
+      // and t+1, which take tiles t+5 and t+6.
+      wait_vmcnt<0>();
+      __syncthreads();
+      issue_tile(t + kNBuf, std::integral_constant<int, s0>{});
+      issue_tile(t + 1 + kNBuf, std::integral_constant<int, s1>{});
+    };
+    for (int t = k_lo;;) {
+      pair(t, std::integral_constant<int, 0>{});
+      if ((t += 2) >= k_hi) break;
+      pair(t, std::integral_constant<int, 2>{});
+      if ((t += 2) >= k_hi) break;
+      pair(t, std::integral_constant<int, 4>{});
+      if ((t += 2) >= k_hi) break;
+      pair(t, std::integral_constant<int, 1>{});
+      if ((t += 2) >= k_hi) break;
+      pair(t, std::integral_constant<int, 3>{});
+      if ((t += 2) >= k_hi) break;
     }
-    l_run += psum;
-    pv(CS, pf);
-  };
-  auto pair = [&](int t, auto S0) __attribute__((always_inline)) {
-    constexpr int s0 = decltype(S0)::value;
-    constexpr int s1 = (s0 + 1) % kNBuf;
-    step(t, std::integral_constant<int, s0>{}, sa, sb);
-    step(t + 1, std::integral_constant<int, s1>{}, sb, sa);
-    // Tiles t+3 and t+4 landed; every wave is done with the slots of tiles t
-    // and t+1, which take tiles t+5 and t+6.
+    // No load may still be writing LDS when the part (or the workgroup) ends.
     wait_vmcnt<0>();
-    __syncthreads();
-    issue_tile(t + kNBuf, std::integral_constant<int, s0>{});
-    issue_tile(t + 1 + kNBuf, std::integral_constant<int, s1>{});
-  };
-  for (int t = k_lo;;) {
-    pair(t, std::integral_constant<int, 0>{});
-    if ((t += 2) >= k_hi) break;
-    pair(t, std::integral_constant<int, 2>{});
-    if ((t += 2) >= k_hi) break;
-    pair(t, std::integral_constant<int, 4>{});
-    if ((t += 2) >= k_hi) break;
-    pair(t, std::integral_constant<int, 1>{});
-    if ((t += 2) >= k_hi) break;
-    pair(t, std::integral_constant<int, 3>{});
-    if ((t += 2) >= k_hi) break;
-  }
-  // No load may still be writing LDS when the part (or the workgroup) ends.
-  wait_vmcnt<0>();
 
-  if (SPLIT && (k_lo > 0 || k_hi < ntiles)) {
-    // A part of a split item.  A run holds at most two partial parts: one
-    // starting inside an item (its first part, side 0) and one starting at
-    // an item's first tile (its last part, side 1).  The parts of an item are
-    // in runs first .. last: side 1 of run first, side 0 of the others.
-    const int side = k_lo > 0 ? 0 : 1;
-    // The workgroups of an item may run on different XCDs, whose L2s are not
-    // coherent with each other: the state goes out through stores that write
-    // through to memory and comes back through loads that bypass the
-    // non-coherent caches (system-coherent cache policy, SC1), so no fence
-    // has to write back or invalidate a whole L2 (which would also evict the
-    // K and V tiles other workgroups are streaming).  Every store is complete
-    // (vmcnt 0) before the barrier and the counter is bumped after it, so the
-    // workgroup that arrives last sees every state.
-    constexpr int kSC1 = 16;  // buffer cache-policy bit
-    const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
-        part + ((size_t)run * 2 + side) * kPartFloats, (short)0, kPartFloats * 4, 0x00020000);
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const floatx16& a = oacc[c >> 2];
-      const int e = 4 * (c & 3);
-      const u32x4 d = {__float_as_uint(a[e]), __float_as_uint(a[e + 1]), __float_as_uint(a[e + 2]),
-                       __float_as_uint(a[e + 3])};
-      __builtin_amdgcn_raw_buffer_store_b128(d, mine, tid * 16, c * kBQ * 2 * 16, kSC1);
-    }
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run), mine, tid * 4, 64 * kBQ * 2 * 4, kSC1);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_run), mine, tid * 4, 65 * kBQ * 2 * 4, kSC1);
-    wait_vmcnt<0>();
-    __syncthreads();
-    int* flag = (int*)ring_lds;  // the count is passed on through the (drained) ring
-    if (tid == 0)
-      flag[0] = __hip_atomic_fetch_add(cnt + item, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int arrived = flag[0];
-    __syncthreads();  // every wave has read the flag before the ring is reused
-    const int t0 = (item - rounds * (int)gridDim.x) * ntiles;  // the item's first leftover unit
-    const int first = t0 / units, last = (t0 + ntiles - 1) / units;
-    if (arrived != last - first) continue;
-    // Last to arrive: merge the other parts' states.
-    for (int j = first; j <= last; ++j) {
-      if (j == run) continue;
-      const __amdgpu_buffer_rsrc_t other = __builtin_amdgcn_make_buffer_rsrc(
-          part + ((size_t)j * 2 + (j == first ? 1 : 0)) * kPartFloats, (short)0, kPartFloats * 4,
-          0x00020000);
-      const float m_o = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(other, tid * 4, 64 * kBQ * 2 * 4, kSC1));
-      const float l_o = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(other, tid * 4, 65 * kBQ * 2 * 4, kSC1));
-      const float m_new = fmaxf(m_run, m_o);
-      const float fa = __builtin_amdgcn_exp2f(m_run - m_new);
-      const float fb = __builtin_amdgcn_exp2f(m_o - m_new);
-      m_run = m_new;
-      l_run = l_run * fa + l_o * fb;
+    if (SPLIT && (k_lo > 0 || k_hi < ntiles)) {
+      // A part of a split item.  A run holds at most two partial parts: one
+      // starting inside an item (its first part, side 0) and one starting at
+      // an item's first tile (its last part, side 1).  The parts of an item are
+      // in runs first .. last: side 1 of run first, side 0 of the others.
+      const int side = k_lo > 0 ? 0 : 1;
+      // The workgroups of an item may run on different XCDs, whose L2s are not
+      // coherent with each other: the state goes out through stores that write
+      // through to memory and comes back through loads that bypass the
+      // non-coherent caches (system-coherent cache policy, SC1), so no fence
+      // has to write back or invalidate a whole L2 (which would also evict the
+      // K and V tiles other workgroups are streaming).  Every store is complete
+      // (vmcnt 0) before the barrier and the counter is bumped after it, so the
+      // workgroup that arrives last sees every state.
+      constexpr int kSC1 = 16;  // buffer cache-policy bit
+      const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
+          part + ((size_t)run * 2 + side) * kPartFloats, (short)0, kPartFloats * 4, 0x00020000);
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
-        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(other, tid * 16, c * kBQ * 2 * 16, kSC1);
-        floatx16& a = oacc[c >> 2];
-        const int e0 = 4 * (c & 3);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a[e0 + e] = a[e0 + e] * fa + __uint_as_float(t[e]) * fb;
+        const floatx16& a = oacc[c >> 2];
+        const int e = 4 * (c & 3);
+        const u32x4 d = {__float_as_uint(a[e]), __float_as_uint(a[e + 1]), __float_as_uint(a[e + 2]),
+                         __float_as_uint(a[e + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(d, mine, tid * 16, c * kBQ * 2 * 16, kSC1);
       }
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run), mine, tid * 4, 64 * kBQ * 2 * 4, kSC1);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_run), mine, tid * 4, 65 * kBQ * 2 * 4, kSC1);
+      wait_vmcnt<0>();
+      __syncthreads();
+      int* flag = (int*)ring_lds;  // the count is passed on through the (drained) ring
+      if (tid == 0)
+        flag[0] = __hip_atomic_fetch_add(cnt + item, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const int arrived = flag[0];
+      __syncthreads();  // every wave has read the flag before the ring is reused
+      const int t0 = (item - rounds * (int)gridDim.x) * ntiles;  // the item's first leftover unit
+      const int first = t0 / units, last = (t0 + ntiles - 1) / units;
+      if (arrived != last - first) continue;
+      // Last to arrive: merge the other parts' states.
+      for (int j = first; j <= last; ++j) {
+        if (j == run) continue;
+        const __amdgpu_buffer_rsrc_t other = __builtin_amdgcn_make_buffer_rsrc(
+            part + ((size_t)j * 2 + (j == first ? 1 : 0)) * kPartFloats, (short)0, kPartFloats * 4,
+            0x00020000);
+        const float m_o =
+            __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(other, tid * 4, 64 * kBQ * 2 * 4, kSC1));
+        const float l_o =
+            __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(other, tid * 4, 65 * kBQ * 2 * 4, kSC1));
+        const float m_new = fmaxf(m_run, m_o);
+        const float fa = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float fb = __builtin_amdgcn_exp2f(m_o - m_new);
+        m_run = m_new;
+        l_run = l_run * fa + l_o * fb;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(other, tid * 16, c * kBQ * 2 * 16, kSC1);
+          floatx16& a = oacc[c >> 2];
+          const int e0 = 4 * (c & 3);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e0 + e] = a[e0 + e] * fa + __uint_as_float(t[e]) * fb;
+        }
+      }
+      if (tid == 0) __hip_atomic_store(cnt + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tid == 0) __hip_atomic_store(cnt + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
 
-  // Normalise and store: lane holds query row lr, dims db*32 + 8 g + 4 lh + 0..3.
-  const float inv = 1.0f / half_sum(l_run);
-  const int orow = qb * kBQ + wave * 32 + lr;
-  if (orow < n) {
-    bf16* op = o + (size_t)orow * ldo + hoff;
+    // Normalise and store: lane holds query row lr, dims db*32 + 8 g + 4 lh + 0..3.
+    const float inv = 1.0f / half_sum(l_run);
+    const int orow = qb * kBQ + wave * 32 + lr;
+    if (orow < n) {
+      bf16* op = o + (size_t)orow * ldo + hoff;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 t;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 t;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = to_bf16(oacc[db][4 * g4 + e] * inv);
-        *(bf16x4*)(op + db * 32 + 8 * g4 + 4 * lh) = t;
-      }
-  }
-  if (!SPLIT) break;
+          for (int e = 0; e < 4; ++e) t[e] = to_bf16(oacc[db][4 * g4 + e] * inv);
+          *(bf16x4*)(op + db * 32 + 8 * g4 + 4 * lh) = t;
+        }
+    }
+    if (!SPLIT) break;
   }  // parts
 }
 
