@@ -38,7 +38,7 @@ TRAFFIC = {
                                                  "gemm.hip": "b53dbdd3828f6dda"}),
     "gemm_out_proj_gated": (746.8e6 + 59.3e6, {"gemm_kernels.hpp": "e24657fca6e19f81",
                                                "gemm.hip": "b53dbdd3828f6dda"}),
-    "attention": (324.7e6 + 89.4e6, {"attention.hip": "37219002a9735f3f"}),
+    "attention": (324.7e6 + 89.4e6, {"attention.hip": "da7350361fcede31"}),
 }
 
 

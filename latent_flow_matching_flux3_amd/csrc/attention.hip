@@ -167,7 +167,7 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
     const int qb = item - head * nqb;
     const int hoff = head * kHeadDim;
 
-    // Q^T fragments of this wave's 32 rows, in registers for the whole kernel:
+    // Q^T fragments of this wave's 32 rows, in registers for the whole part:
     // the B operand of k-step st is query row lr, dims 16 st + 8 lh .. +8.
     bf16x8 qf[8];
     {
