@@ -229,3 +229,13 @@ def latents(seed: int, n: int, name: str = "img") -> torch.Tensor:
 
 def text_features(seed: int, n: int) -> torch.Tensor:
     return normal_bf16((n, TXT_FEAT), 1.0, seed, f"txt.{n}")
+
+
+def stack_inputs(lay: Layout, seed: int):
+    """Inputs of one transformer call on layout `lay`: image latents
+    [n_img, 128], reference latents [n_cond, 128] (None without references)
+    and text features [n_txt, 20480], all bf16 (torch CPU)."""
+    img = latents(seed + 1, lay.n_img)
+    cond = latents(seed + 2, lay.n_cond, "cond") if lay.n_cond else None
+    txt = text_features(seed + 3, lay.n_txt)
+    return img, cond, txt

@@ -38,11 +38,13 @@ function that uses it):
   R12 all references of a sample form one image_cond stream in stage 1.
   R14 attn_out is applied to the attention output (a listed tensor), though
       the blog's block sketch folds it away.
-  R17 fp8r ("rowwise FP8"): each row of a projection's input (per token) and
-      of its weight (per output row) gets scale = row max / 448 and is
-      rounded to OCP E4M3; products accumulate exactly and are scaled after
-      the dot product.  The output projection is one product over [o | swiglu]
-      against [attn_out | mlp_out], so those row scales span both parts.
+  R17 fp8r ("rowwise FP8"): every Linear of the checkpoint is quantized on
+      its own, as a per-tensor checkpoint stores it: its weight per output
+      row and its input per token, scale = row max / 448, codes rounded to
+      OCP E4M3; the dot products are exact and scaled afterwards.  attn_out
+      and mlp_out are two Linears with their own weight scales and their own
+      input scales (o and swiglu); q_proj, k_proj, v_proj and mlp_in read
+      the same input, so they share its codes and scales.
 """
 from __future__ import annotations
 
@@ -293,37 +295,34 @@ def quantize_rows_fp8(x):
 
 
 def fp8r_linear(a: np.ndarray, w: np.ndarray, quant=quantize_rows_fp8) -> np.ndarray:
-    """a w^T with both operands quantized per row (a per token, w per output
-    row), the dot products exact and scaled afterwards (R17)."""
+    """One Linear of the fp8r transformer, a w^T, with its input quantized per
+    row (per token) and its weight per output row, the dot products exact and
+    scaled afterwards (R17)."""
     return quant(a)[2] @ quant(w)[2].T
 
 
 def block_forward_fp8r(x: np.ndarray, segments, mods: np.ndarray, w: dict, ids: np.ndarray,
                        rows=None, quant=quantize_rows_fp8) -> np.ndarray:
-    """block_forward with its two large projections as rowwise-FP8 products
-    (R17): h through [q | k | v | mlp_in] (one activation scale per token, one
-    weight scale per output row of each matrix), and [o | swiglu] through
-    [attn_out | mlp_out] as one product over the 12288 concatenated inputs
-    (one scale per token row and per output row across both).  Everything
-    else as in block_forward."""
+    """block_forward with each of the block's six Linears (q_proj, k_proj,
+    v_proj, mlp_in, attn_out, mlp_out) as a rowwise-FP8 product of its own
+    (R17).  Everything else as in block_forward."""
     n = x.shape[0]
     shift, scale, gate = rows_modulation(n, segments, mods)
     h = modulate(layer_norm(x), shift, scale)
     if rows is None:
         rows = np.arange(n)
-    w_in = np.concatenate([w["q_proj"], w["k_proj"], w["v_proj"], w["mlp_in"]], axis=0)
-    proj = fp8r_linear(h, w_in, quant)                # [n, 3*3072 + 2*9216]
-    q = proj[rows, :HIDDEN].reshape(-1, HEADS, HEAD_DIM)
-    k = proj[:, HIDDEN:2 * HIDDEN].reshape(n, HEADS, HEAD_DIM)
-    v = proj[:, 2 * HIDDEN:3 * HIDDEN].reshape(n, HEADS, HEAD_DIM)
+    hr = h[rows]
+    q = fp8r_linear(hr, w["q_proj"], quant).reshape(-1, HEADS, HEAD_DIM)
+    k = fp8r_linear(h, w["k_proj"], quant).reshape(n, HEADS, HEAD_DIM)
+    v = fp8r_linear(h, w["v_proj"], quant).reshape(n, HEADS, HEAD_DIM)
     q = apply_rope(rms_norm(q, w["norm.query_norm.scale"]), ids[rows])
     k = apply_rope(rms_norm(k, w["norm.key_norm.scale"]), ids)
     o = attention(q, k, v).reshape(-1, HIDDEN)
-    ab = proj[rows, 3 * HIDDEN:]
+    att = fp8r_linear(o, w["attn_out"], quant)
+    ab = fp8r_linear(hr, w["mlp_in"], quant)
     a, b = ab[:, :MLP_HIDDEN], ab[:, MLP_HIDDEN:]
-    cat = np.concatenate([o, silu(a) * b], axis=1)
-    w_out = np.concatenate([w["attn_out"], w["mlp_out"]], axis=1)
-    return x[rows] + gate[rows] * fp8r_linear(cat, w_out, quant)
+    mlp = fp8r_linear(silu(a) * b, w["mlp_out"], quant)
+    return x[rows] + gate[rows] * (att + mlp)
 
 
 # ----------------------------------------------------------------------------

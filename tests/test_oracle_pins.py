@@ -592,9 +592,9 @@ def test_fp8r_linear_exact_on_representable_rows():
 
 
 def test_fp8r_block_structure_matches_block_forward():
-    """With the quantizer replaced by the identity, the fp8r block (one fused
-    input projection, one output projection over [o | swiglu]) is the plain
-    block, which is pinned to torch's layers; with FP8 it stays close."""
+    """With the quantizer replaced by the identity, the fp8r block (six
+    Linears, each a product of its own) is the plain block, which is pinned to
+    torch's layers; with FP8 it stays close."""
     rng = np.random.default_rng(3)
     n = 12
     w = {k: f64(v) for k, v in syn.block_weights(5, "single_blocks.0").items()}
@@ -608,3 +608,73 @@ def test_fp8r_block_structure_matches_block_forward():
     got = O.block_forward_fp8r(x, [(0, n)], mods, w, ids)
     d, r = got - x, ref - x
     assert float((d * r).sum() / np.linalg.norm(d) / np.linalg.norm(r)) > 0.99
+
+
+def test_fp8r_block_quantizes_each_linear_on_its_own():
+    """A per-tensor rowwise checkpoint holds one scale per row of each of the
+    block's tensors ("[Feature] FLUX.3 Image Klein support #2142", Tensor
+    names: q_proj, k_proj, v_proj, attn_out [3072, 3072], mlp_in
+    [18432, 3072], mlp_out [3072, 9216]): the quantizer must see each weight
+    as that tensor and each Linear's own input (h four times, o, swiglu),
+    never a concatenation of two of them."""
+    rng = np.random.default_rng(4)
+    n = 5
+    w = {k: f64(v) for k, v in syn.block_weights(6, "single_blocks.0").items()}
+    x = rng.standard_normal((n, O.HIDDEN))
+    mods = rng.standard_normal((1, 3, O.HIDDEN)) * 0.3
+    seen = []
+
+    def spy(a):
+        a = np.asarray(a, np.float64)
+        seen.append(a)
+        return O.quantize_rows_fp8(a)
+
+    O.block_forward_fp8r(x, [(0, n)], mods, w, O.build_ids(1, 2, 3), quant=spy)
+    shapes = sorted(a.shape for a in seen)
+    want = sorted([(n, O.HIDDEN)] * 5 + [(n, O.MLP_HIDDEN)] +
+                  [w[k].shape for k in ("q_proj", "k_proj", "v_proj", "attn_out", "mlp_in", "mlp_out")])
+    assert shapes == want
+    for k in ("q_proj", "k_proj", "v_proj", "attn_out", "mlp_in", "mlp_out"):
+        assert any(a.shape == w[k].shape and np.array_equal(a, w[k]) for a in seen), k
+
+
+def test_fp8r_output_parts_keep_their_own_scales():
+    """attn_out(o) + mlp_out(swiglu) with o and swiglu at very different
+    magnitudes: per-Linear rowwise scales keep both products exact on
+    E4M3-representable rows, where one scale across [o | swiglu] would round
+    the small part away."""
+    rng = np.random.default_rng(5)
+    grid = O.e4m3_value(np.arange(1, 0x7F))
+
+    def rows(nr, k, lo, hi):
+        v = rng.choice(grid, (nr, k)) * rng.choice([-1.0, 1.0], (nr, k))
+        v[:, 0] = 448.0
+        return v * np.exp2(rng.integers(lo, hi, (nr, 1)))
+
+    o, sw = rows(6, 128, -24, -18), rows(6, 384, 0, 4)
+    wo, wm = rows(8, 128, -10, -6), rows(8, 384, -3, 1)
+    exact = o @ wo.T + sw @ wm.T
+    np.testing.assert_allclose(O.fp8r_linear(o, wo) + O.fp8r_linear(sw, wm), exact, rtol=1e-13)
+    fused = O.fp8r_linear(np.concatenate([o, sw], 1), np.concatenate([wo, wm], 1))
+    assert np.abs(fused - exact).max() > 1e-3 * np.abs(o @ wo.T).max()
+
+
+# ---- sampler update ([issue] Sampling: x += (sigma_{k+1} - sigma_k) v) --------
+
+def test_euler_update_closed_forms():
+    """On the straight path x(s) = (1 - s) x0 + s x1, whose velocity
+    dx/ds = x1 - x0 is constant, the update from sigma to sigma_next lands on
+    x(sigma_next) exactly, step after step, and ends on x0 at sigma = 0; a
+    zero-length step leaves x unchanged; two steps add up to one."""
+    rng = np.random.default_rng(6)
+    x0, x1 = rng.standard_normal((2, 7, 128))
+    v = x1 - x0
+    s = O.sigmas(16)
+    x = x1.copy()
+    for k in range(16):
+        x = O.euler_update(x, v, s[k], s[k + 1])
+        np.testing.assert_allclose(x, (1 - s[k + 1]) * x0 + s[k + 1] * x1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(x, x0, rtol=0, atol=1e-12)
+    assert np.array_equal(O.euler_update(x1, v, 0.37, 0.37), x1)
+    two = O.euler_update(O.euler_update(x1, v, 0.9, 0.6), v, 0.6, 0.2)
+    np.testing.assert_allclose(two, O.euler_update(x1, v, 0.9, 0.2), rtol=0, atol=1e-12)
