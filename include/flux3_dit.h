@@ -130,8 +130,8 @@ int flux3_qk_norm_rope(uint16_t* q, int ldq, uint16_t* k, int ldk, int n, const 
 
 /* ---- a7: attention -------------------------------------------------------------
  * o = softmax(q k^T / sqrt(128)) v per head over all n keys, no mask
- * ([blog] "Two stages": in the joint blocks every token attends to every
- * token; stage-1 calls pass one stream's rows only).
+ * ([blog] "Two stages": the joint blocks run one attention over the whole
+ * concatenated sequence; stage-1 calls pass one stream's rows only).
  *   q, k, v : device [n][24][128] bf16, row strides ldq, ldk, ldv
  *   o       : device output [n][24][128] bf16, row stride ldo
  * fp32 accumulation; probabilities are rounded to bf16 for the P.V product.
@@ -186,12 +186,15 @@ typedef struct flux3_block_weights {
   const uint16_t* q_scale;  /* device [128] bf16 */
   const uint16_t* k_scale;  /* device [128] bf16 */
   /* fp8r ([blog] "Base model and quantized variants": rowwise FP8): when set
-   * (from flux3_pack_block_fp8), the block's two projections run as rowwise
-   * E4M3 products, their inputs quantized per token on the fly. */
+   * (from flux3_pack_block_fp8), the block's six Linears run as rowwise
+   * E4M3 products, each Linear's input quantized per token on the fly and
+   * its weight per output row ([issue] "Tensor names": one scale per row of
+   * each tensor). */
   const uint8_t* w_in_fp8;  /* device [27648][3072] OCP E4M3 codes */
-  const float* w_in_scale;  /* device [27648] fp32 */
-  const uint8_t* w_out_fp8; /* device [3072][12288] */
-  const float* w_out_scale; /* device [3072] */
+  const float* w_in_scale;  /* device [27648] fp32 (row scales of q|k|v|mlp_in) */
+  const uint8_t* w_out_fp8; /* device [3072][12288]: attn_out codes | mlp_out codes */
+  const float* w_out_scale; /* device [3][3072]: attn_out row scales, mlp_out row
+                             * scales, and attn_out's over mlp_out's (fp32) */
 } flux3_block_weights;
 
 #define FLUX3_W_IN_ROWS 27648
@@ -219,8 +222,10 @@ int flux3_quantize_rows_fp8(const uint16_t* x, int ldx, int rows, int cols, uint
                             float* scale, hipStream_t stream);
 
 /* flux3_pack_block_fp8: quantize a packed block's w_in and w_out (from
- * flux3_pack_block) per row into the fp8 fields' buffers (caller-allocated,
- * sizes as in flux3_block_weights). */
+ * flux3_pack_block) into the fp8 fields' buffers (caller-allocated, sizes as
+ * in flux3_block_weights): w_in per row; w_out's first 3072 columns
+ * (attn_out) and its last 9216 (mlp_out) per row as two tensors, plus the
+ * ratio of their row scales. */
 int flux3_pack_block_fp8(const uint16_t* w_in, const uint16_t* w_out, uint8_t* w_in_fp8,
                          float* w_in_scale, uint8_t* w_out_fp8, float* w_out_scale, hipStream_t stream);
 

@@ -267,7 +267,7 @@ class PackedBlock:
             w_in8 = torch.empty((W_IN_ROWS, HIDDEN), dtype=torch.uint8, device=dev)
             w_out8 = torch.empty((HIDDEN, W_OUT_COLS), dtype=torch.uint8, device=dev)
             s_in = torch.empty(W_IN_ROWS, dtype=torch.float32, device=dev)
-            s_out = torch.empty(HIDDEN, dtype=torch.float32, device=dev)
+            s_out = torch.empty(3 * HIDDEN, dtype=torch.float32, device=dev)
             _check(lib().flux3_pack_block_fp8(_ptr(self.w_in), _ptr(self.w_out), _ptr(w_in8), _ptr(s_in),
                                               _ptr(w_out8), _ptr(s_out), _stream(stream)))
             self.fp8 = (w_in8, s_in, w_out8, s_out)
@@ -283,7 +283,7 @@ class PackedBlock:
         w_in8 = torch.empty((W_IN_ROWS, HIDDEN), dtype=torch.uint8, device=dev)
         w_out8 = torch.empty((HIDDEN, W_OUT_COLS), dtype=torch.uint8, device=dev)
         s_in = torch.empty(W_IN_ROWS, dtype=torch.float32, device=dev)
-        s_out = torch.empty(HIDDEN, dtype=torch.float32, device=dev)
+        s_out = torch.empty(3 * HIDDEN, dtype=torch.float32, device=dev)
         _check(lib().flux3_pack_block_fp8(_ptr(self.w_in), _ptr(self.w_out), _ptr(w_in8), _ptr(s_in),
                                           _ptr(w_out8), _ptr(s_out), _stream(stream)))
         b.fp8 = (w_in8, s_in, w_out8, s_out)

@@ -62,8 +62,8 @@ bf16* B(uint16_t* p) { return reinterpret_cast<bf16*>(p); }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Block workspace: xm [n][3072] | qkv [n][9216] | cat [n][12288], bf16, then
-// for fp8 blocks cat8 [n][12288] codes and the two row-scale vectors [n]
-// (the fp8 xm codes reuse the xm region).  The q|k|v region is dead once
+// for fp8 blocks cat8 [n][12288] codes and four row-scale vectors [n]: the
+// input's, o's, h's and o's over h's (the fp8 xm codes reuse the xm region).  The q|k|v region is dead once
 // attention has run, so the output projection borrows it as scratch for a
 // K-split product (sized for that too).
 struct BlockWs {
@@ -73,7 +73,9 @@ struct BlockWs {
   bf16* cat;
   uint8_t* cat8;
   float* scale_in;
-  float* scale_out;
+  float* scale_o;
+  float* scale_h;
+  float* ratio_oh;
   void* attn_split;  // split attention's partial states and counters (or null)
   int attn_counters;
 };
@@ -84,7 +86,7 @@ size_t qkv_region_bytes(int n) {
 
 size_t block_ws_bytes(int n) {
   return align256((size_t)n * kHidden * 2) + qkv_region_bytes(n) + align256((size_t)n * kWOutCols * 2) +
-         align256((size_t)n * kWOutCols) + 2 * align256((size_t)n * 4) + attn_split_ws_bytes(n);
+         align256((size_t)n * kWOutCols) + 4 * align256((size_t)n * 4) + attn_split_ws_bytes(n);
 }
 
 BlockWs carve_block_ws(void* ws, int n) {
@@ -101,7 +103,11 @@ BlockWs carve_block_ws(void* ws, int n) {
   p += align256((size_t)n * kWOutCols);
   w.scale_in = (float*)p;
   p += align256((size_t)n * 4);
-  w.scale_out = (float*)p;
+  w.scale_o = (float*)p;
+  p += align256((size_t)n * 4);
+  w.scale_h = (float*)p;
+  p += align256((size_t)n * 4);
+  w.ratio_oh = (float*)p;
   p += align256((size_t)n * 4);
   w.attn_split = attn_split_ws_bytes(n) ? p : nullptr;
   w.attn_counters = attn_split_counter_count(n);
@@ -212,14 +218,22 @@ void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
   }
   // a8: gated residual
   if (fp8) {
-    launch_quant_rows_fp8(ws.cat, kWOutCols, n, kWOutCols, ws.cat8, kWOutCols, ws.scale_out, st);
+    // attn_out(o) + mlp_out(h): two Linears, each with its own scales, in
+    // one product over [o | h]
+    launch_quant_cat_fp8(ws.cat, kWOutCols, n, ws.cat8, kWOutCols, ws.scale_o, ws.scale_h, ws.ratio_oh,
+                         st);
     GemmArgs o{};
     o.A8 = ws.cat8;
     o.lda = kWOutCols;
     o.B8 = w->w_out_fp8;
     o.ldb = kWOutCols;
-    o.a_scale = ws.scale_out;
-    o.w_scale = w->w_out_scale;
+    o.k_part = kHidden;
+    o.a_scale0 = ws.scale_o;
+    o.a_scale = ws.scale_h;
+    o.a_ratio = ws.ratio_oh;
+    o.w_scale0 = w->w_out_scale;
+    o.w_scale = w->w_out_scale + kHidden;
+    o.w_ratio = w->w_out_scale + 2 * kHidden;
     o.M = n;
     o.N = kHidden;
     o.K = kWOutCols;
@@ -500,7 +514,12 @@ int flux3_pack_block_fp8(const uint16_t* w_in, const uint16_t* w_out, uint8_t* w
   REQUIRE_PTR(w_out_fp8);
   REQUIRE(w_in_scale != nullptr && w_out_scale != nullptr, FLUX3_EINVAL, "scale buffers are null");
   launch_quant_rows_fp8(B(w_in), kHidden, kWInRows, kHidden, w_in_fp8, kHidden, w_in_scale, stream);
-  launch_quant_rows_fp8(B(w_out), kWOutCols, kHidden, kWOutCols, w_out_fp8, kWOutCols, w_out_scale, stream);
+  // attn_out and mlp_out are quantized as the tensors they are, with the
+  // ratio of their row scales for the product over [o | h]
+  launch_quant_rows_fp8(B(w_out), kWOutCols, kHidden, kHidden, w_out_fp8, kWOutCols, w_out_scale, stream);
+  launch_quant_rows_fp8(B(w_out) + kHidden, kWOutCols, kHidden, kMlp, w_out_fp8 + kHidden, kWOutCols,
+                        w_out_scale + kHidden, stream);
+  launch_scale_ratio(w_out_scale, w_out_scale + kHidden, w_out_scale + 2 * kHidden, kHidden, stream);
   return check_launch("pack_block_fp8");
 }
 

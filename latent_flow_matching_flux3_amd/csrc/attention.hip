@@ -1,7 +1,7 @@
 // Flash-style attention forward: o = softmax(q k^T / sqrt(128)) v per head,
-// no mask ("Welcome FLUX.3 Image Klein in Diffusers", §Two stages: in the
-// joint blocks every token attends to every other token; a stage-1 call is
-// simply made on one stream's rows).
+// unmasked over all n rows ("Welcome FLUX.3 Image Klein in Diffusers", §Two
+// stages: the joint blocks put the whole concatenated sequence in one
+// attention; a stage-1 call passes one stream's rows).
 //
 // Design (gfx950, head_dim 128):
 //   - One workgroup = 4 waves = 128 query rows of one head; each wave owns 32

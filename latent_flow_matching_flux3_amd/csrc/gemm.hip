@@ -291,15 +291,4 @@ void launch_gemm(const GemmArgs& g, hipStream_t st) {
   }
 }
 
-// Variant entry used by the tile-shape sweep: cfg selects one instantiation.
-int launch_gemm_variant(const GemmArgs& g, int cfg, hipStream_t st) {
-  switch (cfg) {
-    case 0: run_regs<256, 256, 2, 4>(g, st); return 0;
-    case 1: run_regs<128, 128, 2, 2>(g, st); return 0;
-    case 9: run_ring<256, 256, 2, 2, 32, 4, 1>(g, st); return 0;
-    case 11: run_ring<256, 256, 2, 2, 32, 5, 1>(g, st); return 0;
-  }
-  return -1;
-}
-
 }  // namespace flux3

@@ -26,6 +26,14 @@
 // indices clamped to M-1); the ring's waits have retired them long before
 // the epilogue, which reads them with LDS loads (a global load there would
 // wait for every store in flight).
+//
+// Two Linears side by side along K (k_part > 0: the block's [o | h] against
+// [attn_out | mlp_out], each Linear with its own row and column scales): a
+// work item whose K range lies in one Linear takes that Linear's scales; one
+// that spans both also loads the ratios of the first Linear's scales to the
+// second's, and when its k steps reach k_part it multiplies the accumulators
+// (the first Linear's unscaled products so far) by row ratio x column ratio,
+// which brings them to the second Linear's scales, applied in the epilogue.
 #pragma once
 
 #include "gemm_kernels.hpp"
@@ -50,9 +58,12 @@ void gemm_ring_fp8_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   constexpr int STAGE = (BM + BN) * CPR;  // chunks per buffer (32 KiB)
   constexpr int A_BLK = BM / Lay::RPB / NW, B_BLK = BN / Lay::RPB / NW;
   constexpr int PER = A_BLK + B_BLK;      // loads per wave per slice (8)
-  constexpr int SC_CHUNKS = 96;           // per-wave scale area: 1.5 KiB
+  // Per-wave scale area (floats): [0, 128) row scales, [128, 384) column
+  // scales (+ the copy the 64-lane load writes), [384, 512) row ratios,
+  // [512, 768) column ratios (+ copy): 3 KiB.
+  constexpr int SC_CHUNKS = 192;
   static_assert(T::FM == 4 && T::FN == 4 && PER == 8, "tile geometry");
-  static_assert(STAGES >= 3 && (STAGES - 2) * PER + 3 < 64, "ring depth");
+  static_assert(STAGES >= 3 && (STAGES - 2) * PER + 6 < 64, "ring depth");
   __shared__ bf16x8 lds[STAGES * STAGE + NW * SC_CHUNKS];
 
   const int splits = EPI == GemmEpi::kSplitPartial ? g.ksplit : 1;
@@ -174,7 +185,9 @@ void gemm_ring_fp8_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   // Output origin of the tile being computed, and its scales into this
   // wave's LDS area: rows (clamped to M-1) by two 4-byte loads, columns by
   // one 16-byte load (lanes 32..63 repeat lanes 0..31 into unused bytes).
-  int out_row = 0, out_col = 0;
+  // rescale_at: the k step (even) at which the accumulators move from the
+  // first Linear's scales to the second's, or -1.
+  int out_row = 0, out_col = 0, rescale_at = -1;
   const unsigned sc_lds = lds_base + (unsigned)(STAGES * STAGE + wave * SC_CHUNKS) * 16u;
   auto set_out = [&](int i) {
     int tm, tn, split;
@@ -185,17 +198,60 @@ void gemm_ring_fp8_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     const unsigned ra = 4u * (unsigned)min(r0 + lane, g.M - 1);
     const unsigned rb = 4u * (unsigned)min(r0 + 64 + lane, g.M - 1);
     const unsigned cw = 16u * (unsigned)(lane & 31);
-    const float* ws = g.w_scale + out_col;
+    const int k_begin = __builtin_amdgcn_readfirstlane(split * KT * BKB);
+    const bool first_only = g.k_part > 0 && k_begin + KT * BKB <= g.k_part;
+    const bool spans = g.k_part > k_begin && k_begin + KT * BKB > g.k_part;
+    rescale_at = spans ? (g.k_part - k_begin) / BKB : -1;
+    const float* as = first_only ? g.a_scale0 : g.a_scale;
+    const float* ws = (first_only ? g.w_scale0 : g.w_scale) + out_col;
     asm volatile(
         "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dword %0, %4\n\t"
         "s_add_u32 m0, %3, 256\n\ts_nop 0\n\tglobal_load_lds_dword %1, %4\n\t"
         "s_add_u32 m0, %3, 512\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %5"
-        :: "v"(ra), "v"(rb), "v"(cw), "s"(sc_lds), "s"(g.a_scale), "s"(ws)
+        :: "v"(ra), "v"(rb), "v"(cw), "s"(sc_lds), "s"(as), "s"(ws)
         : "m0");
+    if (spans) {
+      const float* wr = g.w_ratio + out_col;
+      asm volatile(
+          "s_add_u32 m0, %3, 1536\n\ts_nop 0\n\tglobal_load_lds_dword %0, %4\n\t"
+          "s_add_u32 m0, %3, 1792\n\ts_nop 0\n\tglobal_load_lds_dword %1, %4\n\t"
+          "s_add_u32 m0, %3, 2048\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %5"
+          :: "v"(ra), "v"(rb), "v"(cw), "s"(sc_lds), "s"(g.a_ratio), "s"(wr)
+          : "m0");
+    }
   };
   const float* sc = (const float*)(lds + STAGES * STAGE + wave * SC_CHUNKS);
   auto store_tile = [&]() { epilogue<T, EPI, true>(g, acc, out_row, out_col, sc); };
-
+  // The first Linear's products so far, brought to the second's scales
+  // (element r of fragment (i, j): row 32 i + lane % 32, column
+  // 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4 of the wave tile).  Each
+  // accumulator register is read, scaled and written back in place, so the
+  // accumulators never leave their registers.
+  auto rescale = [&]() {
+    const int lr = lane & 31;
+    // the last k step's MFMAs may still be writing these registers: wait
+    // out the longest MFMA-write to VALU-read distance before the first read
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      const float ra = sc[384 + 32 * i + lr];
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 wr = *(const float4*)(sc + 512 + 32 * j + frag_col(g4, lane));
+          const float f[4] = {ra * wr.x, ra * wr.y, ra * wr.z, ra * wr.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float t;
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\ts_nop 0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                         : "+a"(acc[i][j][4 * g4 + e]), "=&v"(t) : "v"(f[e]));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
   // Prologue: slices 0 .. STAGES-1 in flight, wait for slice 0.
   set_src(0);
 #pragma unroll
@@ -246,6 +302,7 @@ void gemm_ring_fp8_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   for (int ti = 0; ti < walk.count; ++ti) {
     set_out(ti);
     for (int kt = 0; kt < KT; kt += 2) {
+      if (kt == rescale_at) rescale();
       slice(P0{});
       slice(P1{});
     }

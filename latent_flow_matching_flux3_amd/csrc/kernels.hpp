@@ -54,6 +54,16 @@ struct GemmArgs {
   const uint8_t* B8;
   const float* a_scale;
   const float* w_scale;
+  // fp8 products over two Linears side by side along K (the block's
+  // [o | h] against [attn_out | mlp_out]): K columns below k_part belong to
+  // the first, whose products are scaled by a_scale0[r] * w_scale0[c]; the
+  // rest by a_scale[r] * w_scale[c].  a_ratio = a_scale0 / a_scale per row
+  // and w_ratio = w_scale0 / w_scale per column (k_part = 0: one Linear).
+  int k_part;
+  const float* a_scale0;
+  const float* w_scale0;
+  const float* a_ratio;
+  const float* w_ratio;
 };
 
 // Scratch bytes a kGatedResidual or kStoreF32 product of this shape uses when
@@ -67,6 +77,13 @@ void launch_ln_modulate_fp8(const float* x, int ldx, uint8_t* out, int ldo, floa
                             const SegTable& seg, const float* mod, int mod_stride, hipStream_t st);
 void launch_quant_rows_fp8(const bf16* x, int ldx, int rows, int cols, uint8_t* out, int ldo,
                            float* scale, hipStream_t st);
+// Rows of the block's [o | h] (12288 wide): the first 3072 and the last 9216
+// values quantized as two rows of their own: codes, scale0 (o), scale1 (h)
+// and ratio = scale0 / scale1 per row.
+void launch_quant_cat_fp8(const bf16* x, int ldx, int rows, uint8_t* out, int ldo, float* scale0,
+                          float* scale1, float* ratio, hipStream_t st);
+// out[i] = a[i] / b[i] (fp32 division), i < n.
+void launch_scale_ratio(const float* a, const float* b, float* out, int n, hipStream_t st);
 
 void launch_ln_modulate(const float* x, int ldx, bf16* out, int ldo, int n, const SegTable& seg,
                         const float* mod, int mod_stride, hipStream_t st);

@@ -6,9 +6,11 @@
 //   - ln_modulate_fp8_kernel: LayerNorm + modulation (as ln_modulate_kernel)
 //     with the quantization of the modulated row fused (the in-projection's
 //     input never exists in bf16);
+//   - quant_cat_fp8_kernel: the out-projection's input [o | h] (12288 wide,
+//     every block), read once into registers, o and h with a scale each
+//     (they feed two Linears, attn_out and mlp_out);
 //   - quant_rows_fp8_reg_kernel: rows of a multiple of 2048 values up to
-//     16384 (the out-projection's input [o | h], 12288 wide, every block),
-//     read once into registers;
+//     16384, read once into registers;
 //   - quant_rows_fp8_kernel: any other width (the weights, once), two passes.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -173,7 +175,84 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_reg_kernel(const bf16* __r
   if (threadIdx.x == 0) out_scale[row] = rs;
 }
 
+// One workgroup per row of the block's [o | h] (6 * 2048 bf16 values, in
+// registers): o (the first kHidden values) and h (the rest) are the inputs
+// of two Linears and get a scale each; ratio = scale of o / scale of h.
+__global__ __launch_bounds__(256) void quant_cat_fp8_kernel(const bf16* __restrict__ x, int ldx,
+                                                            uint8_t* __restrict__ out, int ldo,
+                                                            float* __restrict__ scale0,
+                                                            float* __restrict__ scale1,
+                                                            float* __restrict__ ratio) {
+  constexpr int C = kWOutCols / 2048;
+  constexpr int kSplitChunk = kHidden / 8;  // 8-value chunks of o
+  static_assert(kWOutCols % 2048 == 0 && kHidden % 8 == 0, "row geometry");
+  __shared__ float part[2][4];
+  const int row = blockIdx.x;
+  const bf16* xr = x + (size_t)row * ldx;
+  float v[C][8];
+  float amax0 = 0.f, amax1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    const int chunk = threadIdx.x + 256 * i;
+    const bf16x8 t = *(const bf16x8*)(xr + chunk * 8);
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[i][e] = to_f32(t[e]);
+      m = fmaxf(m, fabsf(v[i][e]));
+    }
+    if (chunk < kSplitChunk) amax0 = fmaxf(amax0, m);
+    else amax1 = fmaxf(amax1, m);
+  }
+  amax0 = wave_max(amax0);
+  amax1 = wave_max(amax1);
+  if ((threadIdx.x & 63) == 0) {
+    part[0][threadIdx.x >> 6] = amax0;
+    part[1][threadIdx.x >> 6] = amax1;
+  }
+  __syncthreads();
+  amax0 = fmaxf(fmaxf(part[0][0], part[0][1]), fmaxf(part[0][2], part[0][3]));
+  amax1 = fmaxf(fmaxf(part[1][0], part[1][1]), fmaxf(part[1][2], part[1][3]));
+  float rs0, inv0, rs1, inv1;
+  row_scale(amax0, rs0, inv0);
+  row_scale(amax1, rs1, inv1);
+  uint8_t* orow = out + (size_t)row * ldo;
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    const int chunk = threadIdx.x + 256 * i;
+    const float inv = chunk < kSplitChunk ? inv0 : inv1;
+    uint2 w;
+    w.x = fp8x4(v[i][0], v[i][1], v[i][2], v[i][3], inv);
+    w.y = fp8x4(v[i][4], v[i][5], v[i][6], v[i][7], inv);
+    *(uint2*)(orow + chunk * 8) = w;
+  }
+  if (threadIdx.x == 0) {
+    scale0[row] = rs0;
+    scale1[row] = rs1;
+    ratio[row] = rs0 / rs1;
+  }
+}
+
+__global__ __launch_bounds__(256) void scale_ratio_kernel(const float* __restrict__ a,
+                                                          const float* __restrict__ b,
+                                                          float* __restrict__ out, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = a[i] / b[i];
+}
+
 }  // namespace
+
+void launch_quant_cat_fp8(const bf16* x, int ldx, int rows, uint8_t* out, int ldo, float* scale0,
+                          float* scale1, float* ratio, hipStream_t st) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(quant_cat_fp8_kernel, dim3(rows), dim3(256), 0, st, x, ldx, out, ldo, scale0, scale1,
+                     ratio);
+}
+
+void launch_scale_ratio(const float* a, const float* b, float* out, int n, hipStream_t st) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(scale_ratio_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a, b, out, n);
+}
 
 void launch_ln_modulate_fp8(const float* x, int ldx, uint8_t* out, int ldo, float* scale, int n,
                             const SegTable& seg, const float* mod, int mod_stride, hipStream_t st) {

@@ -170,7 +170,7 @@ def silu(x: np.ndarray) -> np.ndarray:
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, chunk: int = 512) -> np.ndarray:
     """Per head: softmax(q k^T / sqrt(128)) v over all keys, no mask
-    ([blog] §Two stages: in stage 2 everything attends to everything; the pads
+    ([blog] §Two stages: stage 2 has no mask over the joined sequence; the pads
     are attended too, §From prompt to tokens).  q [Nq,H,d], k/v [Nk,H,d].
     Rows are processed in chunks only to bound memory."""
     nq, nh, d = q.shape
@@ -405,7 +405,7 @@ def stack_forward(W, B, img: np.ndarray, cond, txt: np.ndarray, img_h: int, img_
     ids = build_ids(img_h, img_w, txt.shape[0], refs)
     modes, streams, vecs = stage1(W, B, img, cond, txt, ids, refs, sigma, sigma_next, n_early, block)
 
-    # stage 2: the streams concatenated, every token attends to every token
+    # stage 2: the streams concatenated, one unmasked attention over all rows
     seg = []
     start = 0
     for xs in streams:

@@ -37,8 +37,10 @@ def test_quantize_rows_bit_exact(L, rows, cols):
 
 def test_pack_block_fp8_bit_exact(L):
     """flux3_pack_block_fp8 (through PackedBlock(fp8=True)): the codes and
-    row scales of the packed w_in and w_out equal the oracle's rowwise
-    quantization of the packed bf16 rows (sampled rows of both)."""
+    row scales of the packed w_in equal the oracle's rowwise quantization of
+    its bf16 rows, and those of w_out equal the quantization of attn_out and
+    mlp_out as two tensors ("[Feature] FLUX.3 Image Klein support #2142",
+    Tensor names), with the ratio of their row scales (sampled rows)."""
     w = syn.block_weights(78, "single_blocks.0")
     wd = {k: dev(v) for k, v in w.items()}
     w_in, w_out = L.flux3_pack_block(wd)
@@ -46,11 +48,21 @@ def test_pack_block_fp8_bit_exact(L):
     torch.cuda.synchronize()
     w_in8, s_in, w_out8, s_out = (t.cpu() for t in blk.fp8)
     rng = np.random.default_rng(9)
-    for packed, codes8, scale8, name in [(w_in, w_in8, s_in, "w_in"), (w_out, w_out8, s_out, "w_out")]:
-        rows = np.sort(rng.choice(packed.shape[0], 48, replace=False))
-        codes, scale, _ = O.quantize_rows_fp8(packed[rows].float().cpu().numpy())
-        np.testing.assert_array_equal(codes8[rows].numpy(), codes, err_msg=name)
-        np.testing.assert_array_equal(scale8[rows].numpy(), scale, err_msg=name)
+    rows = np.sort(rng.choice(w_in.shape[0], 48, replace=False))
+    codes, scale, _ = O.quantize_rows_fp8(w_in[rows].float().cpu().numpy())
+    np.testing.assert_array_equal(w_in8[rows].numpy(), codes, err_msg="w_in")
+    np.testing.assert_array_equal(s_in[rows].numpy(), scale, err_msg="w_in")
+    rows = np.sort(rng.choice(w_out.shape[0], 48, replace=False))
+    s_out = s_out.view(3, -1).numpy()
+    scales = []
+    for part, (c0, c1), name in [(0, (0, 3072), "attn_out"), (1, (3072, 12288), "mlp_out")]:
+        src = w[name][rows].float().numpy()
+        np.testing.assert_array_equal(w_out[rows, c0:c1].float().cpu().numpy(), src, err_msg=name)
+        codes, scale, _ = O.quantize_rows_fp8(src)
+        np.testing.assert_array_equal(w_out8[rows, c0:c1].numpy(), codes, err_msg=name)
+        np.testing.assert_array_equal(s_out[part, rows], scale, err_msg=name)
+        scales.append(scale)
+    np.testing.assert_array_equal(s_out[2, rows], scales[0] / scales[1])
 
 
 @pytest.mark.parametrize("m,n,k", [(300, 512, 3072), (513, 256, 256), (64, 27648, 3072), (130, 3072, 12288),
@@ -85,11 +97,14 @@ def _fp8_block_case(L, n, seed, segs):
     return w, x, mods, blk
 
 
-@pytest.mark.parametrize("n,cuts", [(96, [64]), (300, [200, 260]), (600, [])])
+@pytest.mark.parametrize("n,cuts", [(96, [64]), (300, [200, 260]), (600, []), (1300, [1000])])
 def test_block_fp8(L, n, cuts):
     """The block with fp8r projections against the oracle's fp8r block
     (its activation codes come from float64 LayerNorm values, so a few codes
-    may differ by one step from the kernel's fp32 ones)."""
+    may differ by one step from the kernel's fp32 ones).  The output
+    projection's two Linears: 96 and 300 rows split K into ranges that each
+    lie in one Linear; 1300 rows into three ranges, the first spanning both
+    (rescaled at column 3072); 600 rows unsplit (rescaled at 3072)."""
     segs = [0] + cuts + [n]
     seed = 700 + n
     w, x, mods, blk = _fp8_block_case(L, n, seed, segs)
