@@ -239,6 +239,45 @@ def test_attention_ws_plain_sizes(L):
     assert_agree(f64(o), O.attention(q, k, v).reshape(n, 3072), "attention_ws plain")
 
 
+@pytest.mark.parametrize("n,balanced", [(1030, False), (2817, True)])
+def test_attention_rising_scores(L, n, balanced):
+    """Scores that rise from key tile to key tile by more than the online
+    softmax lets its reference max lag (8 in log2 units), up to |s| ~ 1e3:
+    q = a_row e_0 + noise, k = b_key e_0 + noise with b rising along the
+    keys, so rows with a = 8 see their max jump past the reference on every
+    32-key tile (the output accumulator must be rescaled each time, and a
+    missed or inverted rescale overflows or mis-weights), rows with a = -8
+    keep their max in the first tile, a = 0.5 rises slowly, a = 0 is flat.
+    At 2817 rows the balanced schedule merges parts whose reference maxima
+    are hundreds apart."""
+    rise = 30.0 if n < 2000 else 11.0          # log2 units per 32-key tile at a = 8
+    beta = rise / (32 * 8 * math.log2(math.e) / math.sqrt(128))
+    g = torch.Generator().manual_seed(n)
+    a = torch.tensor([8.0, -8.0, 0.5, 0.0]).repeat((n + 3) // 4)[:n]
+    b = 8.0 + beta * torch.arange(n, dtype=torch.float32)
+    q = torch.randn(n, 24, 128, generator=g)
+    k = torch.randn(n, 24, 128, generator=g)
+    q[:, :, 0] = a[:, None]
+    k[:, :, 0] = b[:, None]
+    v = torch.randn(n, 24, 128, generator=g)
+    qkv = torch.cat([q.reshape(n, 3072), k.reshape(n, 3072), v.reshape(n, 3072)], 1).to(torch.bfloat16)
+    qf, kf, vf = (f64(qkv[:, i * 3072:(i + 1) * 3072]).reshape(n, 24, 128) for i in range(3))
+    s_max = np.abs(np.einsum("nhd,nhd->nh", qf, kf)).max() / math.sqrt(128) * math.log2(math.e)
+    say(f"attention rising scores n={n} balanced={balanced} (|s| up to {s_max:.0f} log2 units)")
+    d = dev(qkv)
+    o = torch.empty((n, 3072), dtype=torch.bfloat16, device="cuda")
+    if balanced:
+        ws = L.workspace(L.flux3_attention_workspace_size(n))
+        L.flux3_attention_ws(d[:, :3072], d[:, 3072:6144], d[:, 6144:], o, ws)
+    else:
+        L.flux3_attention(d[:, :3072], d[:, 3072:6144], d[:, 6144:], o)
+    torch.cuda.synchronize()
+    ref = O.attention(qf, kf, vf).reshape(n, 3072)
+    got = f64(o)
+    for r0, what in ((0, "a=8"), (1, "a=-8"), (2, "a=0.5"), (3, "a=0")):
+        assert_agree(got[r0::4], ref[r0::4], f"attention rising n={n} rows {what}")
+
+
 # ---- a3..a8: one block ------------------------------------------------------------------------
 
 def _block_inputs(seed, lay, mod_scale=0.5):
