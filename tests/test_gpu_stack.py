@@ -5,15 +5,24 @@ Weights and inputs are seeded bf16 from flux3_synth; the GPU gets exactly the
 values the oracle reads.  Reduced-depth stacks keep the real widths (hidden
 3072, 24 heads, mlp 9216) and only run fewer blocks; one test runs the full
 5 + 28 depth with all ~5.5 B parameters."""
+import hashlib
+import json
+import os
+import sys
+
 import numpy as np
 import pytest
 import torch
 
 import flux3_synth as syn
 import oracle as O
-from gpu_util import assert_agree, dev, f64, require_gpu, say
+from gpu_util import FP8_REL_MAX, assert_agree, dev, f64, require_gpu, say
 
 pytestmark = pytest.mark.gpu
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+sys.path.insert(0, GOLD)
+import make_stack_golden  # noqa: E402  (fingerprints of the stored cases' inputs)
 
 
 @pytest.fixture(scope="module")
@@ -110,14 +119,21 @@ def test_stack_full_tokens_reduced_depth(L):
     assert_agree(f64(v), ref, f"stack n={lay.n_total} depth 1+1")
 
 
+@pytest.fixture(scope="module")
+def full_t2i(L):
+    """All 5 + 28 blocks of the text-to-image transformer (image and text
+    streams, every checkpoint tensor, ~5.5 B parameters) from seed 7."""
+    say("generating the 5 + 28 block transformer (5.5B parameters)")
+    return Weights(L, 7, syn.WORKLOADS["stack_t2i_1024_4608tok"], 5, 28)
+
+
 @pytest.mark.timeout(900)
-def test_stack_full_depth(L):
+def test_stack_full_depth(L, full_t2i):
     """All 5 + 28 blocks and every checkpoint tensor, at the smallest
     workload (8x8 image tokens + 32 text tokens)."""
     lay = syn.Layout(8, 8, 32)
     seed = 7
-    say("stack full depth n=96: generating 5.5B parameters")
-    wts = Weights(L, seed, lay, 5, 28)
+    wts = full_t2i
     img, cond, txt = _inputs(lay, seed)
     sig, sig_next = np.float32(1.0), np.float32(0.9541)
     say("stack full depth: GPU")
@@ -126,6 +142,72 @@ def test_stack_full_depth(L):
     ref = O.stack_forward(wts.W, wts.B, f64(img), None, f64(txt), lay.img_h, lay.img_w, [],
                           float(sig), float(sig_next), 5, 28)
     assert_agree(f64(v), ref, "stack full depth n=96")
+
+
+def _golden(name):
+    """The oracle's v for a workload too slow to recompute here, written by
+    tests/golden/make_stack_golden.py (which calls only the oracle and the
+    seeded generators), with the case's description and input fingerprint."""
+    with open(os.path.join(GOLD, "stack_golden.json")) as f:
+        meta = json.load(f)[name]
+    path = os.path.join(GOLD, meta["file"])
+    with open(path, "rb") as f:
+        assert hashlib.sha256(f.read()).hexdigest() == meta["sha256"], f"{path} changed"
+    return meta, np.load(path)
+
+
+def _check_fingerprint(meta):
+    fp = make_stack_golden.fingerprint(meta)
+    for k, v in meta["fingerprint"].items():
+        assert fp[k] == pytest.approx(v, rel=1e-12, abs=1e-9), f"seeded input {k} differs from the golden's"
+
+
+@pytest.mark.timeout(900)
+def test_stack_full_depth_t2i_1024(L, full_t2i):
+    """The headline workload: flux3_stack_forward with all 5 + 28 blocks on
+    the 1024^2 text-to-image tokens (64x64 image + 512 text = 4608) in the
+    benchmarked launch (stage 1's side stream, the balanced attention
+    schedule), every row of v against the oracle's (stored)."""
+    meta, ref = _golden("stack_t2i_1024_4608tok_5+28")
+    _check_fingerprint(meta)
+    lay = syn.WORKLOADS[meta["layout"]]
+    img, cond, txt = syn.stack_inputs(lay, meta["seed"])
+    say(f"stack full depth n={lay.n_total}: GPU")
+    v = _gpu_stack(L, full_t2i, lay, img, cond, txt, meta["sigma"], meta["sigma_next"])
+    assert_agree(f64(v), ref, f"stack 5+28 n={lay.n_total}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["stack_i2i_1024_8704tok_1+1", "stack_4ref_1024_20992tok_1+1"])
+def test_stack_references_1024(L, name):
+    """flux3_stack_forward with references at their full size, depth 1 + 1,
+    every row of v against the oracle's (stored): one 1024^2 reference (8704
+    tokens: the image and reference streams' stage-1 attention both on the
+    balanced schedule, on two streams with their own workspaces at once) and
+    four (20,992 tokens, 16,384 reference rows in one stage-1 stream)."""
+    meta, ref = _golden(name)
+    _check_fingerprint(meta)
+    lay = syn.WORKLOADS[meta["layout"]]
+    wts = Weights(L, meta["seed"], lay, meta["n_early"], meta["n_single"])
+    img, cond, txt = syn.stack_inputs(lay, meta["seed"])
+    say(f"stack n={lay.n_total} depth 1+1: GPU")
+    v = _gpu_stack(L, wts, lay, img, cond, txt, meta["sigma"], meta["sigma_next"])
+    assert_agree(f64(v), ref, f"stack n={lay.n_total}")
+
+
+@pytest.mark.timeout(600)
+def test_stack_fp8r_t2i_1024(L):
+    """The fp8r transformer (every block Linear a rowwise-FP8 product of its
+    own) on the 1024^2 text-to-image tokens, depth 1 + 1, every row of v
+    against the oracle's fp8r stack (stored), at the fp8r block bar."""
+    meta, ref = _golden("stack_t2i_1024_4608tok_fp8r_1+1")
+    _check_fingerprint(meta)
+    lay = syn.WORKLOADS[meta["layout"]]
+    wts = Weights(L, meta["seed"], lay, meta["n_early"], meta["n_single"], fp8=True)
+    img, cond, txt = syn.stack_inputs(lay, meta["seed"])
+    say(f"stack fp8r n={lay.n_total} depth 1+1: GPU")
+    v = _gpu_stack(L, wts, lay, img, cond, txt, meta["sigma"], meta["sigma_next"])
+    assert_agree(f64(v), ref, f"stack fp8r n={lay.n_total}", rel_max=FP8_REL_MAX)
 
 
 def test_flow_map_sampler(L):
