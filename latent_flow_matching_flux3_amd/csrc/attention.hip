@@ -106,7 +106,7 @@ constexpr int kPartFloats = 64 * kBQ * 2 + 2 * kBQ * 2;
 // position j % band of XCD band j / band, so neighbouring runs (parts of one
 // item, one head) share an XCD and its L2.  Each part writes its partial state
 // to `part`, and the workgroup that brings cnt[item] to the item's part count
-// merges the others' states into its own, stores the rows and resets the
+// merges all the states in part order, stores the rows and resets the
 // counter.
 template <bool SPLIT>
 __global__ __launch_bounds__(kBQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -453,9 +453,17 @@ void attn_fwd_kernel(const bf16* __restrict__ q, int ldq, const bf16* __restrict
       const int t0 = (item - rounds * (int)gridDim.x) * ntiles;  // the item's first leftover unit
       const int first = t0 / units, last = (t0 + ntiles - 1) / units;
       if (arrived != last - first) continue;
-      // Last to arrive: merge the other parts' states.
+      // Last to arrive: merge every part's state, its own included (read
+      // back), in part order, so the rounding does not depend on which part
+      // finished last.  The start state (reference max -inf, sum 0, O 0)
+      // takes the first part's state over exactly (factors 0 and 1).
+      m_run = -INFINITY;
+      l_run = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[c][e] = 0.f;
       for (int j = first; j <= last; ++j) {
-        if (j == run) continue;
         const __amdgpu_buffer_rsrc_t other = __builtin_amdgcn_make_buffer_rsrc(
             part + ((size_t)j * 2 + (j == first ? 1 : 0)) * kPartFloats, (short)0, kPartFloats * 4,
             0x00020000);
