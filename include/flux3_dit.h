@@ -160,6 +160,27 @@ int flux3_attention_ws(const uint16_t* q, int ldq, const uint16_t* k, int ldk, c
                        int ldv, uint16_t* o, int ldo, int n, void* workspace, size_t ws_bytes,
                        hipStream_t stream);
 
+/* flux3_attention_noalloc: flux3_attention_ws with the workspace in static
+ * device memory of the library instead of a caller buffer, for callers that
+ * cannot allocate device memory (code being captured into a graph, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same operation, kernels
+ * and results as flux3_attention_ws with a workspace.
+ *   q, k, v, o, ld*, n : as flux3_attention
+ * The library holds one static scratch array per GPU of
+ * FLUX3_ATTENTION_SCRATCH_BYTES (about 69 MB: the balanced schedule's
+ * partial states and counters), from the first call on that GPU until the
+ * process ends; it allocates nothing.  The first call on a device looks the
+ * array's address up (hipGetSymbolAddress), so make one call before capturing
+ * a graph.  The array keeps the last call's contents; the counters are
+ * cleared on the stream by each call.  Every call on one GPU shares the
+ * array, so calls that overlap on one GPU (other streams, other threads)
+ * race.  A row count whose schedule would need more scratch than the array
+ * holds is rejected with FLUX3_EUNSUPPORTED (none does: the balanced
+ * schedule is used only below 2048 items). */
+#define FLUX3_ATTENTION_SCRATCH_BYTES ((size_t)512 * 2 * 16896 * 4 + 2048 * 4)
+int flux3_attention_noalloc(const uint16_t* q, int ldq, const uint16_t* k, int ldk, const uint16_t* v,
+                            int ldv, uint16_t* o, int ldo, int n, hipStream_t stream);
+
 /* ---- projections -------------------------------------------------------------
  * flux3_linear: Y = X W^T, fp32 accumulation, rounded to bf16 (or fp32 when
  * y_f32 is set, then y is ignored).

@@ -67,6 +67,7 @@ _SIGS = {
     "flux3_attention": (I, [P, I, P, I, P, I, P, I, I, P]),
     "flux3_attention_workspace_size": (S, [I]),
     "flux3_attention_ws": (I, [P, I, P, I, P, I, P, I, I, P, S, P]),
+    "flux3_attention_noalloc": (I, [P, I, P, I, P, I, P, I, I, P]),
     "flux3_linear": (I, [P, I, P, I, P, I, P, I, I, I, P]),
     "flux3_pack_block": (I, [P, P, P, P, P, P, P, P, P]),
     "flux3_block_in_proj": (I, [P, I, P, P, P, I, P]),
@@ -208,6 +209,12 @@ def flux3_attention_ws(q, k, v, o, workspace, stream=None):
     _check(lib().flux3_attention_ws(_ptr(q), _ld(q), _ptr(k), _ld(k), _ptr(v), _ld(v), _ptr(o), _ld(o),
                                     q.shape[0], _ptr(workspace) if workspace is not None else None,
                                     ws_bytes, _stream(stream)))
+    return o
+
+
+def flux3_attention_noalloc(q, k, v, o, stream=None):
+    _check(lib().flux3_attention_noalloc(_ptr(q), _ld(q), _ptr(k), _ld(k), _ptr(v), _ld(v), _ptr(o),
+                                         _ld(o), q.shape[0], _stream(stream)))
     return o
 
 

@@ -254,6 +254,43 @@ void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
 
 }  // namespace
 
+// Scratch of flux3_attention_noalloc: the balanced attention schedule's
+// workspace (partial softmax states and per-item counters) in static device
+// memory, one copy per GPU, held until the process ends.  In host code
+// `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, once per device (scratch_ptr).
+static __device__ __align__(256) unsigned char scratch[kAttnSplitMaxBytes];
+static_assert(kAttnSplitMaxBytes == FLUX3_ATTENTION_SCRATCH_BYTES, "header's scratch size");
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on each device), or null with the error recorded.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    fail(FLUX3_EHIP, "no current HIP device (or device index >= %d)", kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      fail(FLUX3_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_dev[dev] = p;
+  }
+  return g_scratch_dev[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* flux3_last_error(void) { return g_err; }
@@ -391,6 +428,32 @@ int flux3_attention_ws(const uint16_t* q, int ldq, const uint16_t* k, int ldk, c
   }
   launch_attention(B(q), ldq, B(k), ldk, B(v), ldv, B(o), ldo, n, stream, need ? workspace : nullptr);
   return check_launch("attention");
+}
+
+int flux3_attention_noalloc(const uint16_t* q, int ldq, const uint16_t* k, int ldk, const uint16_t* v,
+                            int ldv, uint16_t* o, int ldo, int n, hipStream_t stream) {
+  REQUIRE(n >= 0, FLUX3_EINVAL, "n=%d", n);
+  if (n == 0) return FLUX3_OK;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(o);
+  REQUIRE_LD(ldq, kHidden);
+  REQUIRE_LD(ldk, kHidden);
+  REQUIRE_LD(ldv, kHidden);
+  REQUIRE_LD(ldo, kHidden);
+  const size_t need = flux3_attention_workspace_size(n);
+  REQUIRE(need <= kAttnSplitMaxBytes, FLUX3_EUNSUPPORTED,
+          "n=%d needs %zu bytes of scratch, more than the static %zu", n, need, kAttnSplitMaxBytes);
+  void* ws = nullptr;
+  if (need) {
+    ws = scratch_ptr();
+    if (ws == nullptr) return FLUX3_EHIP;
+    // the counters must start at zero (a fill kernel, no memset node)
+    launch_zero_ints(attn_split_counters(ws), attn_split_counter_count(n), stream);
+  }
+  launch_attention(B(q), ldq, B(k), ldk, B(v), ldv, B(o), ldo, n, stream, ws);
+  return check_launch("attention_noalloc");
 }
 
 int flux3_linear(const uint16_t* x, int ldx, const uint16_t* w, int ldw, uint16_t* y, int ldy,

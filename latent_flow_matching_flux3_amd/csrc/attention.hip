@@ -549,6 +549,10 @@ SplitPlan attn_split_plan(int n) {
 
 bool attn_split_used(int n) { return n > 0 && attn_split_plan(n).units > 0; }
 
+static_assert(kAttnSplitMaxBytes == (size_t)kSplitSlots * 2 * kPartFloats * sizeof(float) +
+                                        (size_t)4 * kSplitSlots * sizeof(int),
+              "largest split workspace: partial states + counters of < 4 rounds of items");
+
 size_t attn_split_ws_bytes(int n) {
   if (n <= 0 || attn_items(n) <= kSplitSlots) return 0;
   return (size_t)kSplitSlots * 2 * kPartFloats * sizeof(float) +

@@ -102,6 +102,10 @@ void launch_attention(const bf16* q, int ldq, const bf16* k, int ldk, const bf16
 // (attn_split_ws_bytes) is sized for every row count up to n.
 bool attn_split_used(int n);
 size_t attn_split_ws_bytes(int n);
+// The largest workspace the balanced schedule uses, over every n: partial
+// states of 512 runs (two sides of 16896 floats each) plus one counter per
+// item; it runs only below four whole rounds of items (fewer than 2048).
+constexpr size_t kAttnSplitMaxBytes = (size_t)512 * 2 * 16896 * 4 + 2048 * 4;
 int* attn_split_counters(void* ws);
 int attn_split_counter_count(int n);
 void launch_zero_ints(int* p, int n, hipStream_t st);
