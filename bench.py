@@ -31,8 +31,9 @@ METRIC = "DiT step latency (ms) & TFLOP/s at 1024² (4608 tok); % of MI355X bf16
 COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
 
 # HBM bytes per launch at 4608 rows from rocprofv3 FETCH_SIZE + WRITE_SIZE
-# (calibrated against the 1 GiB copy: factors 2.0 and 1.0), with the sources
-# they were measured on; reported only while those sources are unchanged.
+# (calibrated against the 1 GiB copy: factors 2.0 and 1.0), with the code
+# digests (code_digest) of the sources they were measured on; reported only
+# while that code is unchanged.
 TRAFFIC = {
     "gemm_in_proj_swiglu": (1455.7e6 + 169.9e6, {"gemm_kernels.hpp": "e24657fca6e19f81",
                                                  "gemm.hip": "b53dbdd3828f6dda"}),
@@ -42,16 +43,28 @@ TRAFFIC = {
 }
 
 
-def measured_traffic(kernel: str):
+def code_digest(path: str) -> str:
+    """Digest of a source file's code: comments and whitespace removed, so an
+    edit of a comment keeps it and any change of the code changes it."""
     import hashlib
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return hashlib.sha256(re.sub(r"\s+", "", text).encode()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """The rocprofv3 bytes of `kernel`, if its sources' code is the code they
+    were measured on, else None."""
     if kernel not in TRAFFIC:
         return None
     nbytes, sources = TRAFFIC[kernel]
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "latent_flow_matching_flux3_amd", "csrc")
     for name, digest in sources.items():
-        with open(os.path.join(csrc, name), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest()[:16] != digest:
-                return None
+        if code_digest(os.path.join(csrc, name)) != digest:
+            return None
     return nbytes
 
 
@@ -86,6 +99,11 @@ def parse():
                     help="skip the stack step at the longest sequence (10 references, 49,136 tokens)")
     ap.add_argument("--no-sampler-loop", action="store_true",
                     help="skip the timing of the 16-step loop as one call (eager and graph)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (one block at 96 / 4608 / 8704 tokens, "
+                         "the stack step with four references at 20,992 tokens)")
+    ap.add_argument("--probe", action="store_true",
+                    help="only the peak probes (register-only bf16 MFMA, HBM copy)")
     ap.add_argument("--only", default=None,
                     help="in_proj | out_proj | attention | ln_modulate | qk_norm_rope | copy")
     ap.add_argument("--seed", type=int, default=0)
@@ -152,6 +170,30 @@ def kernel_fixtures(L, torch, blk, table, n_img: int, n: int):
         "gemm_out_proj_gated": (lambda: L.flux3_block_out_proj(cat, blk.w_out, xs, segs, mod),
                                 2.0 * n * (HIDDEN + MLP) * HIDDEN, "flop"),
     }
+
+
+def cold_fixtures(L, torch, blk, table, n_img: int, n: int, sets: int = 4):
+    """The memory-bound kernels of kernel_fixtures, each call on the next of
+    `sets` copies of its buffers (together well past the 256 MB Infinity
+    Cache), so back-to-back calls find their inputs in HBM, not in a cache."""
+    g = torch.Generator(device="cuda").manual_seed(2)
+    xs = [torch.randn((n, HIDDEN), device="cuda", generator=g) for _ in range(sets)]
+    xm = [torch.empty((n, HIDDEN), dtype=torch.bfloat16, device="cuda") for _ in range(sets)]
+    qk = [torch.randn((n, 2 * HIDDEN), device="cuda", generator=g).to(torch.bfloat16) for _ in range(sets)]
+    tables = [table.clone() for _ in range(sets)]
+    mod = torch.randn((2, 3, HIDDEN), device="cuda", generator=g) * 0.1
+    segs = [0, n_img, n]
+    state = {"ln": 0, "qk": 0}
+
+    def ln():
+        i = state["ln"] = (state["ln"] + 1) % sets
+        L.flux3_ln_modulate(xs[i], xm[i], segs, mod)
+
+    def qk_norm():
+        i = state["qk"] = (state["qk"] + 1) % sets
+        L.flux3_qk_norm_rope(qk[i][:, :HIDDEN], qk[i][:, HIDDEN:], blk.q_scale, blk.k_scale, tables[i])
+
+    return {"ln_modulate": ln, "qk_norm_rope": qk_norm}
 
 
 def event_time_ms(torch, fn, reps: int) -> float:
@@ -299,6 +341,103 @@ def long_step(L, torch, syn, model, seed: int, steps: int = 2):
             "tflop_per_step": round(flops / 1e12, 1), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
 
 
+def probe_peaks(torch):
+    """What this GPU sustains: register-only bf16 MFMA (one wave per SIMD,
+    8 independent accumulator chains, random operands) and streaming copies
+    of 2 GiB (HBM read + write: the probe copy on 512, 768 and 1024
+    workgroups, and torch's elementwise multiply, the best of them), each the
+    median of 5 timed launches after a warm-up (libflux3_probe.so)."""
+    import ctypes as C
+    lib = C.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)), "latent_flow_matching_flux3_amd",
+                              "libflux3_probe.so"))
+    lib.flux3_probe_mfma_bf16.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    lib.flux3_probe_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 40000
+    out = torch.empty(cus * 256, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def mfma():
+        assert lib.flux3_probe_mfma_bf16(cus, iters, out.data_ptr(), st.cuda_stream) == 0
+
+    nbytes = 2 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t_mfma = median_event_ms(torch, mfma, 5)
+    copies = {}
+    for blocks in (512, 768, 1024):
+        def copy(b=blocks):
+            assert lib.flux3_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, b, st.cuda_stream) == 0
+        copies[f"probe_copy_{blocks}wg"] = round(2.0 * nbytes / (median_event_ms(torch, copy, 5) * 1e-3) / 1e9, 1)
+    assert torch.equal(src[:1 << 20], dst[:1 << 20])
+    copies["torch_mul"] = round(2.0 * nbytes / (median_event_ms(torch, lambda: torch.mul(src, 1.0, out=dst), 5)
+                                                 * 1e-3) / 1e9, 1)
+    flop = cus * 4 * iters * 8 * 32768.0
+    del src, dst
+    return {"mfma_bf16_tflops": round(flop / (t_mfma * 1e-3) / 1e12, 1),
+            "hbm_copy_gbs": max(copies.values()), "copies_gbs": copies,
+            "vendor": {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS},
+            "how": f"register-only v_mfma_f32_32x32x16_bf16, {cus} workgroups x 4 waves x {iters} x 8; "
+                   f"copies of {nbytes >> 30} GiB; median of 5"}
+
+
+def median_event_ms(torch, fn, reps: int, flush=None) -> float:
+    """Median duration of fn() over reps launches, each between its own HIP
+    events on the current stream; flush() (untimed) runs before each."""
+    import statistics
+    st = torch.cuda.current_stream()
+    fn()
+    times = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        fn()
+        b.record(st)
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    return statistics.median(times)
+
+
+def config_lines(L, torch, syn, model, seed: int):
+    """The other workloads: one joint block at 96 (128^2 px), 4608 (1024^2
+    t2i) and 8704 tokens (1024^2 with one 1024^2 reference), each the median
+    of 20 launches, and one stack step with four 1024^2 references (20,992
+    tokens), the median of 3."""
+    out = {}
+    blk = model.single[0]
+    for name in ("block_128px_96tok", "block_t2i_1024_4608tok", "block_i2i_1024_8704tok"):
+        lay = syn.WORKLOADS[name]
+        n = lay.n_total
+        segs = [0] + [b for _, _, b in lay.segments()]
+        table = L.flux3_rope_table(L.flux3_build_ids(lay.img_h, lay.img_w, lay.n_txt, lay.refs).to("cuda"))
+        x = torch.randn((n, HIDDEN), device="cuda", generator=torch.Generator(device="cuda").manual_seed(seed))
+        mod = torch.randn((len(segs) - 1, 3, HIDDEN), device="cuda",
+                          generator=torch.Generator(device="cuda").manual_seed(seed + 1)) * 0.1
+        ws = L.workspace(L.flux3_block_workspace_size(n))
+        ms = median_event_ms(torch, lambda: L.flux3_block_forward(x, segs, mod, blk, table, ws), 20)
+        assert torch.isfinite(x).all().item(), "non-finite block output"
+        f = block_flops(n)
+        out[name] = {"tokens": n, "ms": round(ms, 4), "gflop": round(f / 1e9, 1),
+                     "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
+        del ws
+    name = "stack_4ref_1024_20992tok"
+    lay = syn.WORKLOADS[name]
+    img, cond, txt = (t.to("cuda") for t in syn.stack_inputs(lay, seed + 12))
+    table = L.flux3_rope_table(L.flux3_build_ids(lay.img_h, lay.img_w, lay.n_txt, lay.refs).to("cuda"))
+    ws = L.workspace(L.flux3_stack_workspace_size(lay.n_img, lay.n_cond, lay.n_txt))
+    v = torch.empty((lay.n_img, 128), dtype=torch.float32, device="cuda")
+    sig = L.flux3_sigmas(16).tolist()
+    ms = median_event_ms(torch, lambda: L.flux3_stack_forward(model, img, cond, txt, table, sig[0], sig[1], v, ws), 3)
+    assert torch.isfinite(v).all().item(), "non-finite velocity"
+    f = stack_flops(lay.n_img, lay.n_cond, lay.n_txt)
+    out[name] = {"tokens": lay.n_total, "ms_per_step": round(ms, 2), "tflop_per_step": round(f / 1e12, 1),
+                 "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
+    del ws
+    return out
+
+
 def cpu_baseline(seed: int):
     """The CPU oracle (float64 NumPy), untuned, on a bounded sample: one joint
     block at 4608 tokens (image 64x64 + 512 text), two modulation segments."""
@@ -362,6 +501,9 @@ def main():
     L.lib()
     if args.only:
         return run_only(args, L, torch, syn)
+    if args.probe:
+        print(json.dumps({"peaks": probe_peaks(torch)}), flush=True)
+        return 0
     lay = syn.WORKLOADS["stack_t2i_1024_4608tok"]
     n_img, n_txt = lay.n_img, lay.n_txt
     n = n_img + n_txt
@@ -391,14 +533,19 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t0 = time.perf_counter()
     e0.record(st)
     for k in range(args.steps):
         step(k)
+        marks[k].record(st)
     e1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
+    import statistics
+    step_ms = [e0.elapsed_time(marks[0])] + [marks[k - 1].elapsed_time(marks[k]) for k in range(1, args.steps)]
+    median_ms = statistics.median(step_ms)
     assert torch.isfinite(v).all().item(), "non-finite velocity"
     flops = stack_flops(n_img, 0, n_txt)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -407,12 +554,20 @@ def main():
     print("[bench] per-kernel timing", file=sys.stderr, flush=True)
     fx = kernel_fixtures(L, torch, model.single[0], table, n_img, n)
     per_kernel = {}
+    cold_fx = cold_fixtures(L, torch, model.single[0], table, n_img, n)
     for name, (fn, work, unit) in fx.items():
         kms = event_time_ms(torch, fn, args.kernel_reps)
+        med = median_event_ms(torch, fn, args.kernel_reps)
         if unit == "flop":
-            per_kernel[name] = {"ms": round(kms, 4), "tflops": round(work / kms / 1e9, 1)}
+            per_kernel[name] = {"ms": round(kms, 4), "tflops": round(work / kms / 1e9, 1),
+                                "median_ms": round(med, 4)}
         else:
-            per_kernel[name] = {"ms": round(kms, 4), "gbs": round(work / kms / 1e6, 1)}
+            per_kernel[name] = {"ms": round(kms, 4), "gbs": round(work / kms / 1e6, 1), "median_ms": round(med, 4)}
+            if name in cold_fx:
+                cms = event_time_ms(torch, cold_fx[name], args.kernel_reps)
+                per_kernel[name].update({"hbm_ms": round(cms, 4), "hbm_gbs": round(work / cms / 1e6, 1),
+                                         "hbm_frac": round(work / cms / 1e6 / PEAK_HBM_GBS, 3)})
+    del cold_fx
     torch.cuda.synchronize()
     # Dominant kernel: most time per step.  The joint blocks dominate (28 of
     # 38 block calls, at the largest row count); each block calls every
@@ -455,6 +610,16 @@ def main():
         print("[bench] stack step at the longest sequence (49,136 tokens)", file=sys.stderr, flush=True)
         long_ctx = long_step(L, torch, syn, model, args.seed)
 
+    configs = None
+    if not args.no_configs:
+        print("[bench] blocks at 96 / 4608 / 8704 tokens, stack step at 20,992 tokens", file=sys.stderr, flush=True)
+        configs = config_lines(L, torch, syn, model, args.seed + 20)
+
+    print("[bench] peak probes", file=sys.stderr, flush=True)
+    peaks = probe_peaks(torch)
+    roof["frac_of_probe_peak"] = round(roof["achieved"] / (peaks["mfma_bf16_tflops"] if roof["unit"] == "TFLOP/s"
+                                                           else peaks["hbm_copy_gbs"]), 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle, one block)", file=sys.stderr, flush=True)
@@ -468,6 +633,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
+        "median_ms_per_step": round(median_ms, 3),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 3),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "steps_per_s": round(1e3 / ms, 3),
@@ -481,7 +647,9 @@ def main():
                    "blocks": "5 per-stream + 28 joint", "params": "5.55B", "tflop_per_step": round(flops / 1e12, 3),
                    "sampler": "flow map, 16-step shifted schedule (alpha 6.93)", "parallelism": "none (1 GPU)"},
         "roofline": roof,
+        "peaks": peaks,
         "kernels": per_kernel,
+        "configs": configs,
         "sampler_loop": loops,
         "fp8r": fp8,
         "cfg_base": cfg,

@@ -3,7 +3,9 @@
     python -m latent_flow_matching_flux3_amd.build [--jobs N] [--verbose]
 
 Every .hip file under csrc/ is compiled to an object in _build/ (parallel
-hipcc processes), then linked into latent_flow_matching_flux3_amd/libflux3_dit.so.
+hipcc processes), then linked into latent_flow_matching_flux3_amd/libflux3_dit.so;
+probe/probe.hip (the measurement harness's peak probes) becomes
+latent_flow_matching_flux3_amd/libflux3_probe.so.
 """
 from __future__ import annotations
 
@@ -64,12 +66,32 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "probe.hip")
+PROBE_LIB = os.path.join(PKG, "libflux3_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The peak probes of the measurement harness (MFMA and HBM copy), a
+    library of their own next to libflux3_dit.so."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *COMMON_FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        probe = ex.submit(build_probe, verbose)
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        probe.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
