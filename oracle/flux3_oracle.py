@@ -45,6 +45,11 @@ function that uses it):
       and mlp_out are two Linears with their own weight scales and their own
       input scales (o and swiglu); q_proj, k_proj, v_proj and mlp_in read
       the same input, so they share its codes and scales.
+
+Parity unpinned against the trained checkpoint: R5 (which head dims a RoPE
+pair rotates) and R9 (SiLU before `lin`) are readings no page fixes and no
+trained weights or reference outputs exist to check them; apply_rope and
+modulation are pinned only to the pages' parameters and to invariants.
 """
 from __future__ import annotations
 
