@@ -459,9 +459,30 @@ def cpu_baseline(seed: int):
     O.block_forward(x, segs, mods, w, ids)
     dt = time.perf_counter() - t0
     fl = block_flops(lay.n_total)
+    # the 128^2 px block (96 tokens) on all cores and on one thread
+    small = syn.WORKLOADS["block_128px_96tok"]
+    ids_s = O.build_ids(small.img_h, small.img_w, small.n_txt)
+    xs = syn.block_activations(seed + 1, small.n_total).to(torch.float64).numpy()
+    segs_s = [(a, b) for _, a, b in small.segments()]
+    t0 = time.perf_counter()
+    O.block_forward(xs, segs_s, mods, w, ids_s)
+    dt_s = time.perf_counter() - t0
+    dt_s1 = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            O.block_forward(xs, segs_s, mods, w, ids_s)
+            dt_s1 = time.perf_counter() - t0
+    except ImportError:
+        pass
+    fl_s = block_flops(small.n_total)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"one joint block at {lay.n_total} tokens ({fl / 1e12:.2f} TFLOP), float64 NumPy, "
-                      f"{dt:.2f} s; the full step is {stack_flops(4096, 0, 512) / 1e12:.1f} TFLOP"}
+                      f"{dt:.2f} s; the full step is {stack_flops(4096, 0, 512) / 1e12:.1f} TFLOP",
+            "block_96tok_ms": {"all_cores": round(dt_s * 1e3, 1),
+                               "one_thread": None if dt_s1 is None else round(dt_s1 * 1e3, 1),
+                               "gflop": round(fl_s / 1e9, 1)}}
 
 
 def run_only(args, L, torch, syn):
