@@ -14,6 +14,7 @@ every row of v with the stored one.
 
 Cases (layouts from flux3_synth.WORKLOADS):
   stack_t2i_1024_4608tok_5+28   1024^2 text-to-image, all 5 + 28 blocks
+  stack_4ref_1024_20992tok_5+28 four 1024^2 references (20,992 tokens), all 5 + 28 blocks
   stack_i2i_1024_8704tok_1+1    1024^2 image-to-image, one 1024^2 reference
   stack_4ref_1024_20992tok_1+1  four 1024^2 references (20,992 tokens)
   stack_t2i_1024_4608tok_fp8r_1+1  the rowwise-FP8 transformer at 1024^2
@@ -52,6 +53,9 @@ CASES = {
     "stack_t2i_1024_4608tok_5+28": dict(layout="stack_t2i_1024_4608tok", seed=7, n_early=5,
                                         n_single=28, sigma=_f32(_S16[3]), sigma_next=_f32(_S16[4]),
                                         block="bf16"),
+    "stack_4ref_1024_20992tok_5+28": dict(layout="stack_4ref_1024_20992tok", seed=7, n_early=5,
+                                          n_single=28, sigma=_f32(_S16[2]), sigma_next=_f32(_S16[3]),
+                                          block="bf16"),
     "stack_i2i_1024_8704tok_1+1": dict(layout="block_i2i_1024_8704tok", seed=23, n_early=1,
                                        n_single=1, sigma=_f32(_S16[8]), sigma_next=_f32(_S16[9]),
                                        block="bf16"),

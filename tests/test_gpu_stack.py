@@ -120,20 +120,21 @@ def test_stack_full_tokens_reduced_depth(L):
 
 
 @pytest.fixture(scope="module")
-def full_t2i(L):
-    """All 5 + 28 blocks of the text-to-image transformer (image and text
-    streams, every checkpoint tensor, ~5.5 B parameters) from seed 7."""
+def full_model(L):
+    """All 5 + 28 blocks of the transformer with every stream's stage-1
+    blocks (image, image_cond, text: every checkpoint tensor, ~5.5 B
+    parameters) from seed 7."""
     say("generating the 5 + 28 block transformer (5.5B parameters)")
-    return Weights(L, 7, syn.WORKLOADS["stack_t2i_1024_4608tok"], 5, 28)
+    return Weights(L, 7, syn.WORKLOADS["stack_4ref_1024_20992tok"], 5, 28)
 
 
 @pytest.mark.timeout(900)
-def test_stack_full_depth(L, full_t2i):
+def test_stack_full_depth(L, full_model):
     """All 5 + 28 blocks and every checkpoint tensor, at the smallest
     workload (8x8 image tokens + 32 text tokens)."""
     lay = syn.Layout(8, 8, 32)
     seed = 7
-    wts = full_t2i
+    wts = full_model
     img, cond, txt = _inputs(lay, seed)
     sig, sig_next = np.float32(1.0), np.float32(0.9541)
     say("stack full depth: GPU")
@@ -163,7 +164,7 @@ def _check_fingerprint(meta):
 
 
 @pytest.mark.timeout(900)
-def test_stack_full_depth_t2i_1024(L, full_t2i):
+def test_stack_full_depth_t2i_1024(L, full_model):
     """The headline workload: flux3_stack_forward with all 5 + 28 blocks on
     the 1024^2 text-to-image tokens (64x64 image + 512 text = 4608) in the
     benchmarked launch (stage 1's side stream, the balanced attention
@@ -173,7 +174,23 @@ def test_stack_full_depth_t2i_1024(L, full_t2i):
     lay = syn.WORKLOADS[meta["layout"]]
     img, cond, txt = syn.stack_inputs(lay, meta["seed"])
     say(f"stack full depth n={lay.n_total}: GPU")
-    v = _gpu_stack(L, full_t2i, lay, img, cond, txt, meta["sigma"], meta["sigma_next"])
+    v = _gpu_stack(L, full_model, lay, img, cond, txt, meta["sigma"], meta["sigma_next"])
+    assert_agree(f64(v), ref, f"stack 5+28 n={lay.n_total}")
+
+
+@pytest.mark.timeout(900)
+def test_stack_full_depth_4ref_1024(L, full_model):
+    """The longest configuration at full depth: flux3_stack_forward with all
+    5 + 28 blocks on four 1024^2 references + a 1024^2 image + 512 text tokens
+    (20,992 tokens; the 16,384-row reference stream through its own five
+    stage-1 blocks on the side stream), every row of v against the oracle's
+    (stored)."""
+    meta, ref = _golden("stack_4ref_1024_20992tok_5+28")
+    _check_fingerprint(meta)
+    lay = syn.WORKLOADS[meta["layout"]]
+    img, cond, txt = syn.stack_inputs(lay, meta["seed"])
+    say(f"stack full depth n={lay.n_total}: GPU")
+    v = _gpu_stack(L, full_model, lay, img, cond, txt, meta["sigma"], meta["sigma_next"])
     assert_agree(f64(v), ref, f"stack 5+28 n={lay.n_total}")
 
 
