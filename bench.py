@@ -33,9 +33,11 @@ COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
 # HBM bytes per launch at 4608 rows from rocprofv3 FETCH_SIZE + WRITE_SIZE
 # (calibrated against the 1 GiB copy: factors 2.0 and 1.0), with the code
 # digests (code_digest) of the sources they were measured on; reported only
-# while that code is unchanged.
+# while that code is unchanged.  The in-projection's figure is the mean over
+# its 4608-row launches inside stack steps (as its roofline is timed); the
+# others are of their kernel alone (--only).
 TRAFFIC = {
-    "gemm_in_proj_swiglu": (1486.3e6 + 169.9e6, {"gemm_kernels.hpp": "654cfe900862b048", "gemm.hip": "13dc9a45230ef548",
+    "gemm_in_proj_swiglu": (1462.8e6 + 169.9e6, {"gemm_kernels.hpp": "654cfe900862b048", "gemm.hip": "13dc9a45230ef548",
                                                  "kernels.hpp": "ddcdbe768eab9041", "common.hpp": "a628a66ce9fdd5dc"}),
     "gemm_out_proj_gated": (748.3e6 + 59.3e6, {"gemm_kernels.hpp": "654cfe900862b048", "gemm.hip": "13dc9a45230ef548",
                                                "kernels.hpp": "ddcdbe768eab9041", "common.hpp": "a628a66ce9fdd5dc"}),
@@ -102,6 +104,11 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (one block at 96 / 4608 / 8704 tokens, "
                          "the stack step with four references at 20,992 tokens)")
+    ap.add_argument("--no-fixtures", action="store_true",
+                    help="skip the per-kernel fixture timing (each kernel alone, back to back)")
+    ap.add_argument("--no-kernel-timer", action="store_true",
+                    help="time the steps without the library's launch timer (the roofline then "
+                         "comes from the back-to-back fixtures)")
     ap.add_argument("--probe", action="store_true",
                     help="only the peak probes (register-only bf16 MFMA, HBM copy)")
     ap.add_argument("--only", default=None,
@@ -138,6 +145,42 @@ def build_model(L, torch, seed: int, n_early: int = 5, n_single: int = 28):
     early = {m: [make_block(L, torch, rnd) for _ in range(n_early)] for m in syn.MODES}
     single = [make_block(L, torch, rnd) for _ in range(n_single)]
     return L.ModelWeights(glob, early, single)
+
+
+# The launch timer's kinds, the name of the kernel each one times, and its
+# algorithmic work per launch of r rows (unit as in kernel_fixtures).
+TIMED = {
+    "in_proj": ("gemm_in_proj_swiglu", lambda r: 2.0 * r * HIDDEN * (3 * HIDDEN + 2 * MLP), "flop"),
+    "qk_norm_rope": ("qk_norm_rope", lambda r: 8.0 * r * HIDDEN + 512.0 * r, "byte"),
+    "attention": ("attention", lambda r: 4.0 * r * r * HIDDEN, "flop"),
+    "out_proj": ("gemm_out_proj_gated", lambda r: 2.0 * r * (HIDDEN + MLP) * HIDDEN, "flop"),
+    "ln_modulate": ("ln_modulate", lambda r: 6.0 * r * HIDDEN, "byte"),
+}
+
+
+def in_stack_kernels(records, steps: int):
+    """Launch-timer records [(kind, rows, ms)] of the timed steps, summarised
+    per kernel and row count: launches, average ms, rate."""
+    out = {}
+    for kind, rows, ms in records:
+        name, work, unit = TIMED[kind]
+        k = out.setdefault(name, {"ms_per_step": 0.0, "rows": {}})
+        k["ms_per_step"] += ms / steps
+        r = k["rows"].setdefault(str(rows), {"launches": 0, "ms": 0.0})
+        r["launches"] += 1
+        r["ms"] += ms
+    for name, k in out.items():
+        _, work, unit = next(v for v in TIMED.values() if v[0] == name)
+        k["ms_per_step"] = round(k["ms_per_step"], 3)
+        for rows, r in k["rows"].items():
+            avg = r.pop("ms") / r["launches"]
+            r["avg_ms"] = round(avg, 4)
+            rate = work(int(rows)) / (avg * 1e-3)
+            if unit == "flop":
+                r["tflops"] = round(rate / 1e12, 1)
+            else:
+                r["gbs"] = round(rate / 1e9, 1)
+    return out
 
 
 def kernel_fixtures(L, torch, blk, table, n_img: int, n: int):
@@ -567,6 +610,25 @@ def main():
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # The library's launch timer records HIP events around launches of the
+    # block's kernels, on the stream each runs on.  First an untimed pass of
+    # the same steps with all five kernels timed (where a step's time goes,
+    # which kernel dominates); then the timed steps with the dominant kernel's
+    # launches timed (two event packets per launch; all five kinds at once
+    # would add ≈1.7% to the step).
+    in_stack = None
+    timed_kind = None
+    timer_cap = args.steps * 6 * (5 + 5 + 28) + 64
+    if not args.no_kernel_timer:
+        nb = max(1, min(args.steps, 5))
+        L.flux3_timer_start(TIMED, timer_cap)
+        for k in range(nb):
+            step(k)
+        torch.cuda.synchronize()
+        in_stack = in_stack_kernels(L.flux3_timer_stop(timer_cap), nb)
+        in_stack["steps"] = nb
+        timed_kind = max((k for k in TIMED), key=lambda k: in_stack[TIMED[k][0]]["ms_per_step"])
+        L.flux3_timer_start([timed_kind], timer_cap)
     t0 = time.perf_counter()
     e0.record(st)
     for k in range(args.steps):
@@ -575,6 +637,9 @@ def main():
     e1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    timed = None
+    if timed_kind is not None:
+        timed = in_stack_kernels(L.flux3_timer_stop(timer_cap), args.steps)[TIMED[timed_kind][0]]
     ms = e0.elapsed_time(e1) / args.steps
     import statistics
     step_ms = [e0.elapsed_time(marks[0])] + [marks[k - 1].elapsed_time(marks[k]) for k in range(1, args.steps)]
@@ -584,11 +649,12 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
 
     # Per-kernel timing at the joint-block shape (4608 rows), same stream.
-    print("[bench] per-kernel timing", file=sys.stderr, flush=True)
     fx = kernel_fixtures(L, torch, model.single[0], table, n_img, n)
     per_kernel = {}
-    cold_fx = cold_fixtures(L, torch, model.single[0], table, n_img, n)
-    for name, (fn, work, unit) in fx.items():
+    cold_fx = {} if args.no_fixtures else cold_fixtures(L, torch, model.single[0], table, n_img, n)
+    if not args.no_fixtures:
+        print("[bench] per-kernel timing", file=sys.stderr, flush=True)
+    for name, (fn, work, unit) in ({} if args.no_fixtures else fx).items():
         kms = event_time_ms(torch, fn, args.kernel_reps)
         med = median_event_ms(torch, fn, args.kernel_reps)
         if unit == "flop":
@@ -602,20 +668,30 @@ def main():
                                          "hbm_frac": round(work / cms / 1e6 / PEAK_HBM_GBS, 3)})
     del cold_fx
     torch.cuda.synchronize()
-    # Dominant kernel: most time per step.  The joint blocks dominate (28 of
-    # 38 block calls, at the largest row count); each block calls every
-    # kernel once, so the longest kernel is the dominant one.
-    dom = max(per_kernel, key=lambda k: per_kernel[k]["ms"])
+    # Dominant kernel: most time per step.  With the launch timer: its
+    # launches at the joint block's 4608 rows inside the timed steps (28 per
+    # step); without it: its back-to-back fixture at 4608 rows.
+    if timed:
+        dom = TIMED[timed_kind][0]
+        dom_ms = timed["rows"][str(n)]["avg_ms"]
+        dom_launches = timed["rows"][str(n)]["launches"]
+        basis = (f"HIP events around each of its {dom_launches} launches at {n} rows in the "
+                 f"{args.steps} timed steps (the library's launch timer, on the launch's stream)")
+    else:
+        dom = max(per_kernel, key=lambda k: per_kernel[k]["ms"])
+        dom_ms = per_kernel[dom]["ms"]
+        basis = f"HIP events around {args.kernel_reps} back-to-back launches at {n} rows"
     dom_work, dom_unit = fx[dom][1], fx[dom][2]
     if dom_unit == "flop":
-        achieved = dom_work / (per_kernel[dom]["ms"] * 1e-3) / 1e12
+        achieved = dom_work / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(dom)}
     else:
-        achieved = dom_work / (per_kernel[dom]["ms"] * 1e-3) / 1e9
+        achieved = dom_work / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    roof.update({"avg_ms": round(dom_ms, 4), "work_per_launch": dom_work, "measured": basis})
 
     loops = None
     if not args.no_sampler_loop:
@@ -681,7 +757,8 @@ def main():
                    "sampler": "flow map, 16-step shifted schedule (alpha 6.93)", "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "peaks": peaks,
-        "kernels": per_kernel,
+        "kernels_in_stack": in_stack,
+        "kernels": per_kernel or None,
         "configs": configs,
         "sampler_loop": loops,
         "fp8r": fp8,

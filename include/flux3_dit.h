@@ -443,6 +443,37 @@ int flux3_sample_cfg(const flux3_model_weights* w, float* x, int n_img, const ui
  *   out: host [steps+1] fp32 (computed in fp64). */
 int flux3_sigmas(int steps, double alpha, float* out);
 
+/* ---- launch timing (profiling) -------------------------------------------------------
+ * Measures the block's kernels where they actually run: inside
+ * flux3_block_forward, flux3_stack_forward(_cfg) and flux3_sample(_cfg), on
+ * whichever stream each launch is made (the caller's, or the library's own
+ * stage-1 side stream).  Not a step of the pages' method: an instrument for
+ * per-kernel rooflines of a whole stack step.
+ *
+ * flux3_timer_start: arm the timer for the kinds in the bit mask `kinds`
+ * (1 << FLUX3_TIMER_*) and up to `capacity` launches.  Creates 2 x capacity
+ * timing HIP events.  While armed, each launch of an armed kind records one
+ * event before it and one after it on its stream; launches past `capacity`
+ * and launches on a stream under graph capture are not recorded.  One timer
+ * per process; FLUX3_EINVAL if it is already armed, kinds is 0 or capacity is
+ * outside 1..1048576.  Recording adds two event packets per timed launch to
+ * the stream.
+ *
+ * flux3_timer_stop: disarm, wait for every recorded event, and write per
+ * launch, in launch order: ms[i] = elapsed time between its two events,
+ * kind[i] = FLUX3_TIMER_*, rows[i] = the rows (tokens) of the launch.
+ * Host arrays of `capacity` entries (each may be NULL); *count = entries
+ * written, min(launches recorded, capacity).  Destroys the events and
+ * disarms even when it fails.  FLUX3_EINVAL if the timer is not armed;
+ * FLUX3_EHIP if an event could not be read (its entry is 0). */
+#define FLUX3_TIMER_IN_PROJ 0       /* a4 + a5: the fused input projection */
+#define FLUX3_TIMER_QK_NORM_ROPE 1  /* a6 */
+#define FLUX3_TIMER_ATTENTION 2     /* a7, every row group of the call */
+#define FLUX3_TIMER_OUT_PROJ 3      /* a8, with its split-K reduce when one runs */
+#define FLUX3_TIMER_LN_MODULATE 4   /* a3 */
+int flux3_timer_start(unsigned kinds, int capacity);
+int flux3_timer_stop(float* ms, int* kind, int* rows, int capacity, int* count);
+
 #ifdef __cplusplus
 }
 #endif

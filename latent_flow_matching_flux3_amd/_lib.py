@@ -89,6 +89,8 @@ _SIGS = {
     "flux3_linear_fp8": (I, [P, I, P, P, I, P, P, P, I, I, I, I, P]),
     "flux3_euler_step": (I, [P, P, P, I, F, F, P]),
     "flux3_sigmas": (I, [I, C.c_double, P]),
+    "flux3_timer_start": (I, [C.c_uint, I]),
+    "flux3_timer_stop": (I, [P, P, P, I, C.POINTER(I)]),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -461,6 +463,29 @@ def flux3_sigmas(steps: int, alpha: float = 6.93) -> torch.Tensor:
     out = torch.empty(steps + 1, dtype=torch.float32)
     _check(lib().flux3_sigmas(steps, float(alpha), out.data_ptr()))
     return out
+
+
+TIMER_KINDS = {"in_proj": 0, "qk_norm_rope": 1, "attention": 2, "out_proj": 3, "ln_modulate": 4}
+
+
+def flux3_timer_start(kinds, capacity: int):
+    """Arm the launch timer for the named kinds (keys of TIMER_KINDS)."""
+    mask = 0
+    for k in kinds:
+        mask |= 1 << TIMER_KINDS[k]
+    _check(lib().flux3_timer_start(mask, int(capacity)))
+
+
+def flux3_timer_stop(capacity: int):
+    """Disarm; returns [(kind name, rows, ms)] per recorded launch, in launch order."""
+    ms = (C.c_float * capacity)()
+    kind = (I * capacity)()
+    rows = (I * capacity)()
+    n = I(0)
+    _check(lib().flux3_timer_stop(C.addressof(ms), C.addressof(kind), C.addressof(rows), int(capacity),
+                                  C.byref(n)))
+    names = {v: k for k, v in TIMER_KINDS.items()}
+    return [(names[kind[i]], rows[i], ms[i]) for i in range(n.value)]
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

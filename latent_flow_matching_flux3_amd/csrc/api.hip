@@ -7,7 +7,9 @@
 
 #include <algorithm>
 #include <cmath>
+#include <atomic>
 #include <mutex>
+#include <new>
 
 #include "../../include/flux3_dit.h"
 #include "common.hpp"
@@ -130,6 +132,50 @@ int check_block_weights(const flux3_block_weights* w) {
   return FLUX3_OK;
 }
 
+// Launch timer (flux3_timer_start / flux3_timer_stop): while armed, a
+// TimedLaunch around a launch of an armed kind records one event before and
+// one after it on the launch's stream.  `kinds` is read without the lock on
+// every launch (0 when disarmed); slots are taken under the lock.
+struct LaunchTimer {
+  std::mutex mu;
+  std::atomic<unsigned> kinds{0};
+  hipEvent_t* ev = nullptr;  // [2 * capacity]: begin, end of slot i at 2i, 2i+1
+  int* kind = nullptr;
+  int* rows = nullptr;
+  int capacity = 0;
+  int count = 0;
+};
+LaunchTimer g_timer;
+
+class TimedLaunch {
+ public:
+  TimedLaunch(int kind, int rows, hipStream_t st) {
+    if ((g_timer.kinds.load(std::memory_order_acquire) & (1u << kind)) == 0) return;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+    std::lock_guard<std::mutex> lock(g_timer.mu);
+    if ((g_timer.kinds.load(std::memory_order_relaxed) & (1u << kind)) == 0 ||
+        g_timer.count >= g_timer.capacity)
+      return;
+    const int i = g_timer.count;
+    if (hipEventRecord(g_timer.ev[2 * i], st) != hipSuccess) return;
+    g_timer.kind[i] = kind;
+    g_timer.rows[i] = rows;
+    g_timer.count = i + 1;
+    end_ = g_timer.ev[2 * i + 1];
+    st_ = st;
+  }
+  ~TimedLaunch() {
+    if (end_ != nullptr) (void)hipEventRecord(end_, st_);
+  }
+  TimedLaunch(const TimedLaunch&) = delete;
+  TimedLaunch& operator=(const TimedLaunch&) = delete;
+
+ private:
+  hipEvent_t end_ = nullptr;
+  hipStream_t st_ = nullptr;
+};
+
 // a4 + a5: [q | k | v] and h_mlp = silu(a) * b in one product over w_in.
 void in_proj(const bf16* xm, int n, const bf16* w_in, bf16* qkv, bf16* h, int ldh, hipStream_t st) {
   GemmArgs g{};
@@ -181,7 +227,10 @@ void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
   uint8_t* const xm8 = (uint8_t*)ws.xm;
   if (fp8) {
     // a3 with the rowwise FP8 quantization fused; a4 + a5 as an fp8r product
-    launch_ln_modulate_fp8(x, kHidden, xm8, kHidden, ws.scale_in, n, seg, mod, 3 * kHidden, st);
+    {
+      TimedLaunch t(FLUX3_TIMER_LN_MODULATE, n, st);
+      launch_ln_modulate_fp8(x, kHidden, xm8, kHidden, ws.scale_in, n, seg, mod, 3 * kHidden, st);
+    }
     GemmArgs g{};
     g.A8 = xm8;
     g.lda = kHidden;
@@ -197,24 +246,35 @@ void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
     g.ldc = 3 * kHidden;
     g.H = ws.cat + kHidden;
     g.ldh = kWOutCols;
+    TimedLaunch t(FLUX3_TIMER_IN_PROJ, n, st);
     launch_gemm_fp8(g, st);
   } else {
     // a3: h = (1 + scale) LN(x) + shift
-    launch_ln_modulate(x, kHidden, ws.xm, kHidden, n, seg, mod, 3 * kHidden, st);
+    {
+      TimedLaunch t(FLUX3_TIMER_LN_MODULATE, n, st);
+      launch_ln_modulate(x, kHidden, ws.xm, kHidden, n, seg, mod, 3 * kHidden, st);
+    }
     // a4 + a5: q | k | v into qkv; SwiGLU output into the last 9216 columns of cat
+    TimedLaunch t(FLUX3_TIMER_IN_PROJ, n, st);
     in_proj(ws.xm, n, B(w->w_in), ws.qkv, ws.cat + kHidden, kWOutCols, st);
   }
   // a6: RMSNorm + RoPE on q and k
-  launch_qk_norm_rope(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, n, B(w->q_scale),
-                      B(w->k_scale), table, st, attn_split_counters(ws.attn_split), ws.attn_counters);
+  {
+    TimedLaunch t(FLUX3_TIMER_QK_NORM_ROPE, n, st);
+    launch_qk_norm_rope(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, n, B(w->q_scale),
+                        B(w->k_scale), table, st, attn_split_counters(ws.attn_split), ws.attn_counters);
+  }
   // a7: attention -> first 3072 columns of cat, per row group
-  const int ng = attn ? attn->n : 1;
-  for (int gi = 0; gi < ng; ++gi) {
-    const int r0 = attn ? attn->off[gi] : 0, r1 = attn ? attn->off[gi + 1] : n;
-    if (r1 <= r0) continue;
-    const bf16* q = ws.qkv + (size_t)r0 * 3 * kHidden;
-    launch_attention(q, 3 * kHidden, q + kHidden, 3 * kHidden, q + 2 * kHidden, 3 * kHidden,
-                     ws.cat + (size_t)r0 * kWOutCols, kWOutCols, r1 - r0, st, ws.attn_split);
+  {
+    const int ng = attn ? attn->n : 1;
+    TimedLaunch t(FLUX3_TIMER_ATTENTION, n, st);
+    for (int gi = 0; gi < ng; ++gi) {
+      const int r0 = attn ? attn->off[gi] : 0, r1 = attn ? attn->off[gi + 1] : n;
+      if (r1 <= r0) continue;
+      const bf16* q = ws.qkv + (size_t)r0 * 3 * kHidden;
+      launch_attention(q, 3 * kHidden, q + kHidden, 3 * kHidden, q + 2 * kHidden, 3 * kHidden,
+                       ws.cat + (size_t)r0 * kWOutCols, kWOutCols, r1 - r0, st, ws.attn_split);
+    }
   }
   // a8: gated residual
   if (fp8) {
@@ -246,8 +306,10 @@ void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
     o.seg = seg;
     o.split_ws = ws.qkv;
     o.split_ws_bytes = ws.qkv_bytes;
+    TimedLaunch t(FLUX3_TIMER_OUT_PROJ, n, st);
     launch_gemm_fp8(o, st);
   } else {
+    TimedLaunch t(FLUX3_TIMER_OUT_PROJ, n, st);
     out_proj(ws.cat, n, B(w->w_out), x, seg, mod, st, ws.qkv, ws.qkv_bytes);
   }
 }
@@ -1039,6 +1101,65 @@ int flux3_sigmas(int steps, double alpha, float* out) {
     const double t = 1.0 - (double)k / steps;
     out[k] = (float)(alpha * t / (1.0 + (alpha - 1.0) * t));
   }
+  return FLUX3_OK;
+}
+
+int flux3_timer_start(unsigned kinds, int capacity) {
+  REQUIRE(kinds != 0 && kinds < (1u << 5), FLUX3_EINVAL, "kinds=0x%x", kinds);
+  REQUIRE(capacity >= 1 && capacity <= (1 << 20), FLUX3_EINVAL, "capacity=%d", capacity);
+  std::lock_guard<std::mutex> lock(g_timer.mu);
+  REQUIRE(g_timer.ev == nullptr, FLUX3_EINVAL, "the launch timer is already armed");
+  hipEvent_t* ev = new (std::nothrow) hipEvent_t[2 * (size_t)capacity]();
+  int* kind = new (std::nothrow) int[capacity];
+  int* rows = new (std::nothrow) int[capacity];
+  int made = 0;
+  hipError_t e = hipSuccess;
+  if (ev != nullptr && kind != nullptr && rows != nullptr)
+    for (; made < 2 * capacity; ++made)
+      if ((e = hipEventCreate(&ev[made])) != hipSuccess) break;
+  if (ev == nullptr || kind == nullptr || rows == nullptr || made < 2 * capacity) {
+    for (int i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
+    delete[] ev;
+    delete[] kind;
+    delete[] rows;
+    return fail(FLUX3_EHIP, "timer events: %s", e != hipSuccess ? hipGetErrorString(e) : "out of host memory");
+  }
+  g_timer.ev = ev;
+  g_timer.kind = kind;
+  g_timer.rows = rows;
+  g_timer.capacity = capacity;
+  g_timer.count = 0;
+  g_timer.kinds.store(kinds, std::memory_order_release);
+  return FLUX3_OK;
+}
+
+int flux3_timer_stop(float* ms, int* kind, int* rows, int capacity, int* count) {
+  REQUIRE(capacity >= 0, FLUX3_EINVAL, "capacity=%d", capacity);
+  std::lock_guard<std::mutex> lock(g_timer.mu);
+  REQUIRE(g_timer.ev != nullptr, FLUX3_EINVAL, "the launch timer is not armed");
+  g_timer.kinds.store(0, std::memory_order_release);
+  const int n = g_timer.count;
+  hipError_t err = hipSuccess;
+  for (int i = 0; i < n; ++i) {
+    hipError_t e = hipEventSynchronize(g_timer.ev[2 * i + 1]);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, g_timer.ev[2 * i], g_timer.ev[2 * i + 1]);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    if (i < capacity) {
+      if (ms) ms[i] = t;
+      if (kind) kind[i] = g_timer.kind[i];
+      if (rows) rows[i] = g_timer.rows[i];
+    }
+  }
+  for (int i = 0; i < 2 * g_timer.capacity; ++i) (void)hipEventDestroy(g_timer.ev[i]);
+  delete[] g_timer.ev;
+  delete[] g_timer.kind;
+  delete[] g_timer.rows;
+  g_timer.ev = nullptr;
+  g_timer.kind = g_timer.rows = nullptr;
+  g_timer.capacity = g_timer.count = 0;
+  if (count) *count = std::min(n, capacity);
+  REQUIRE(err == hipSuccess, FLUX3_EHIP, "timer events: %s", hipGetErrorString(err));
   return FLUX3_OK;
 }
 

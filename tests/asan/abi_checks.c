@@ -93,6 +93,16 @@ int main(void) {
   CHECK(flux3_attention_ws(P16, 3072, P16, 3072, P16, 3072, P16, 3072, 4608, NULL, (size_t)1 << 30, NULL) ==
         FLUX3_EINVAL);
 
+  /* launch timer: argument checks (no HIP call on these paths) */
+  {
+    int cnt = -1;
+    CHECK(flux3_timer_stop(NULL, NULL, NULL, 0, &cnt) == FLUX3_EINVAL);
+    CHECK(flux3_timer_start(0, 10) == FLUX3_EINVAL);
+    CHECK(flux3_timer_start(1u << 5, 10) == FLUX3_EINVAL);
+    CHECK(flux3_timer_start(1u << FLUX3_TIMER_IN_PROJ, 0) == FLUX3_EINVAL);
+    CHECK(flux3_timer_start(1u << FLUX3_TIMER_IN_PROJ, (1 << 20) + 1) == FLUX3_EINVAL);
+  }
+
   /* stack and sampler: missing weights, workspace too small */
   {
     flux3_model_weights mw;

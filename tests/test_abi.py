@@ -90,6 +90,12 @@ def test_error_codes(L):
     segs = (C.c_int * 2)(0, 10)
     assert lib.flux3_block_forward(16, 10, segs, 1, 16, C.byref(w), 16, 16, 100, None) == L.EWORKSPACE
     assert lib.flux3_block_forward(16, 10, segs, 1, 16, C.byref(w), 16, None, 1 << 30, None) == L.EWORKSPACE
+    # launch timer: not armed, no kinds, unknown kind, capacity out of range
+    cnt = C.c_int(-1)
+    assert lib.flux3_timer_stop(None, None, None, 0, C.byref(cnt)) == L.EINVAL
+    assert lib.flux3_timer_start(0, 10) == L.EINVAL
+    assert lib.flux3_timer_start(1 << 5, 10) == L.EINVAL
+    assert lib.flux3_timer_start(1, 0) == L.EINVAL and lib.flux3_timer_start(1, (1 << 20) + 1) == L.EINVAL
     # empty inputs are a no-op
     assert lib.flux3_attention(None, 3072, None, 3072, None, 3072, None, 3072, 0, None) == L.OK
     assert lib.flux3_attention_ws(None, 3072, None, 3072, None, 3072, None, 3072, 0, None, 0, None) == L.OK

@@ -446,3 +446,60 @@ def test_stack_fp8r(L):
     # to the oracle's fp8r result than FP8 quantization itself moves it.
     assert 1 - c_gpu <= 1 - c_q and r_gpu <= r_q, (c_gpu, r_gpu, c_q, r_q)
     assert_agree(f64(v), ref, "stack fp8r", cos_min=0.999, rel_max=FP8_REL_MAX)
+
+
+def test_launch_timer(L):
+    """The launch timer records the block's five kernels in every block call of
+    a stack step, with the call's rows, on the stream each runs on (the text
+    stream's stage-1 block on the side stream), and leaves the results
+    unchanged; it stops at its capacity and records nothing under graph
+    capture."""
+    lay = syn.Layout(8, 12, 40)  # 96 image + 40 text rows
+    seed = 71
+    say("launch timer: stack 96 + 40 rows, depth 1+2")
+    wts = Weights(L, seed, lay, 1, 2)
+    img, _, txt = _inputs(lay, seed)
+    img_d, txt_d = dev(img), dev(txt)
+    table = L.flux3_rope_table(L.flux3_build_ids(lay.img_h, lay.img_w, lay.n_txt).to("cuda"))
+    ws = L.workspace(L.flux3_stack_workspace_size(lay.n_img, 0, lay.n_txt))
+    v = torch.empty((lay.n_img, 128), dtype=torch.float32, device="cuda")
+
+    def run():
+        L.flux3_stack_forward(wts.model, img_d, None, txt_d, table, 0.7, 0.5, v, ws)
+
+    run()
+    torch.cuda.synchronize()
+    plain = v.clone()
+    kinds = list(L.TIMER_KINDS)
+    L.flux3_timer_start(kinds, 64)
+    run()
+    recs = L.flux3_timer_stop(64)
+    assert torch.equal(v, plain), "the timer changed the result"
+    order = ["ln_modulate", "in_proj", "qk_norm_rope", "attention", "out_proj"]
+    # stage 1: the image block (96 rows) and the text block (40 rows, side
+    # stream); stage 2: two joint blocks (136 rows)
+    assert sorted((k, r) for k, r, _ in recs) == sorted((k, r) for r in (96, 40, 136, 136) for k in order)
+    assert [k for k, r, _ in recs if r != 40] == order * 3
+    assert [k for k, r, _ in recs if r == 40] == order
+    assert all(ms > 0 for _, _, ms in recs)
+    say("launch timer: capacity")
+    L.flux3_timer_start(["in_proj", "attention"], 3)
+    run()
+    recs = L.flux3_timer_stop(3)
+    assert [(k, r) for k, r, _ in recs] == [("in_proj", 96), ("attention", 96), ("in_proj", 40)]
+    say("launch timer: graph capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    L.flux3_timer_start(kinds, 64)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    assert L.flux3_timer_stop(64) == []
+    v.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(v, plain), "the captured step differs from the eager one"
