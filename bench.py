@@ -37,11 +37,11 @@ COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
 # its 4608-row launches inside stack steps (as its roofline is timed); the
 # others are of their kernel alone (--only).
 TRAFFIC = {
-    "gemm_in_proj_swiglu": (1462.8e6 + 169.9e6, {"gemm_kernels.hpp": "654cfe900862b048", "gemm.hip": "13dc9a45230ef548",
-                                                 "kernels.hpp": "ddcdbe768eab9041", "common.hpp": "a628a66ce9fdd5dc"}),
-    "gemm_out_proj_gated": (748.3e6 + 59.3e6, {"gemm_kernels.hpp": "654cfe900862b048", "gemm.hip": "13dc9a45230ef548",
-                                               "kernels.hpp": "ddcdbe768eab9041", "common.hpp": "a628a66ce9fdd5dc"}),
-    "attention": (360.0e6 + 90.1e6, {"attention.hip": "bbd9a581ae964ab5", "kernels.hpp": "ddcdbe768eab9041", "common.hpp": "a628a66ce9fdd5dc"}),
+    "gemm_in_proj_swiglu": (1442.3e6 + 169.9e6, {"gemm_kernels.hpp": "9b99c63a15916818", "gemm.hip": "9ead6f0e5bdd6ad8",
+                                                 "kernels.hpp": "0548d5d1c5b3415e", "common.hpp": "a628a66ce9fdd5dc"}),
+    "gemm_out_proj_gated": (746.8e6 + 59.3e6, {"gemm_kernels.hpp": "9b99c63a15916818", "gemm.hip": "9ead6f0e5bdd6ad8",
+                                               "kernels.hpp": "0548d5d1c5b3415e", "common.hpp": "a628a66ce9fdd5dc"}),
+    "attention": (356.9e6 + 89.9e6, {"attention.hip": "bbd9a581ae964ab5", "kernels.hpp": "0548d5d1c5b3415e", "common.hpp": "a628a66ce9fdd5dc"}),
 }
 
 

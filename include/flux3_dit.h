@@ -292,7 +292,10 @@ int flux3_block_out_proj(const uint16_t* cat, int n, const uint16_t* w_out, floa
  *   seg_off  : host [n_seg+1] row offsets; segment s uses mod + s*9216
  *              (shift, scale, gate) fp32 (device)
  *   table    : device rope table of these n rows
- *   workspace: device, >= flux3_block_workspace_size(n) bytes
+ *   workspace: device, >= flux3_block_workspace_size(n) bytes, sized for the
+ *              current device (its CU count fixes the output projection's
+ *              stream-K split); no initial contents needed, and calls that
+ *              share a workspace must not overlap
  * Attention covers all n rows: a stage-1 call passes one stream's rows.
  */
 size_t flux3_block_workspace_size(int n);

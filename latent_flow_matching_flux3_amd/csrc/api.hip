@@ -80,6 +80,14 @@ struct BlockWs {
   float* ratio_oh;
   void* attn_split;  // split attention's partial states and counters (or null)
   int attn_counters;
+  // the output projection's stream-K counters and partial products (or null)
+  int* sk_cnt;
+  float* sk_part;
+  size_t sk_bytes;
+  // counters qk_norm_rope clears before each attention and output projection:
+  // the attention's (when split) and the stream-K ones, one contiguous range
+  int* zero;
+  int nzero;
 };
 
 size_t qkv_region_bytes(int n) {
@@ -88,7 +96,8 @@ size_t qkv_region_bytes(int n) {
 
 size_t block_ws_bytes(int n) {
   return align256((size_t)n * kHidden * 2) + qkv_region_bytes(n) + align256((size_t)n * kWOutCols * 2) +
-         align256((size_t)n * kWOutCols) + 4 * align256((size_t)n * 4) + attn_split_ws_bytes(n);
+         align256((size_t)n * kWOutCols) + 4 * align256((size_t)n * 4) + attn_split_ws_bytes(n) +
+         gemm_sk_ws_bytes(n, kHidden, kWOutCols);
 }
 
 BlockWs carve_block_ws(void* ws, int n) {
@@ -113,6 +122,14 @@ BlockWs carve_block_ws(void* ws, int n) {
   p += align256((size_t)n * 4);
   w.attn_split = attn_split_ws_bytes(n) ? p : nullptr;
   w.attn_counters = attn_split_counter_count(n);
+  p += attn_split_ws_bytes(n);
+  w.sk_bytes = gemm_sk_ws_bytes(n, kHidden, kWOutCols);
+  const int sk_counters = gemm_sk_counters(n, kHidden, kWOutCols);
+  w.sk_cnt = w.sk_bytes ? (int*)p : nullptr;
+  w.sk_part = w.sk_bytes ? (float*)(p + align256((size_t)sk_counters * 4)) : nullptr;
+  // attention counters end where the stream-K counters begin
+  w.zero = w.attn_split ? attn_split_counters(w.attn_split) : w.sk_cnt;
+  w.nzero = w.zero ? (int)(((char*)(w.sk_bytes ? (char*)w.sk_part : p) - (char*)w.zero) / 4) : 0;
   return w;
 }
 
@@ -196,7 +213,8 @@ void in_proj(const bf16* xm, int n, const bf16* w_in, bf16* qkv, bf16* h, int ld
 
 // a8: x += gate * ([o | h] [W_o | W_out]^T).
 void out_proj(const bf16* cat, int n, const bf16* w_out, float* x, const SegTable& seg,
-              const float* mod, hipStream_t st, void* scratch = nullptr, size_t scratch_bytes = 0) {
+              const float* mod, hipStream_t st, void* scratch = nullptr, size_t scratch_bytes = 0,
+              const BlockWs* ws = nullptr) {
   GemmArgs o{};
   o.A = cat;
   o.lda = kWOutCols;
@@ -214,6 +232,11 @@ void out_proj(const bf16* cat, int n, const bf16* w_out, float* x, const SegTabl
   o.seg = seg;
   o.split_ws = scratch;
   o.split_ws_bytes = scratch_bytes;
+  if (ws != nullptr) {
+    o.sk_cnt = ws->sk_cnt;
+    o.sk_part = ws->sk_part;
+    o.sk_bytes = ws->sk_bytes;
+  }
   launch_gemm(o, st);
 }
 
@@ -262,7 +285,7 @@ void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
   {
     TimedLaunch t(FLUX3_TIMER_QK_NORM_ROPE, n, st);
     launch_qk_norm_rope(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, n, B(w->q_scale),
-                        B(w->k_scale), table, st, attn_split_counters(ws.attn_split), ws.attn_counters);
+                        B(w->k_scale), table, st, ws.zero, ws.nzero);
   }
   // a7: attention -> first 3072 columns of cat, per row group
   {
@@ -310,7 +333,7 @@ void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
     launch_gemm_fp8(o, st);
   } else {
     TimedLaunch t(FLUX3_TIMER_OUT_PROJ, n, st);
-    out_proj(ws.cat, n, B(w->w_out), x, seg, mod, st, ws.qkv, ws.qkv_bytes);
+    out_proj(ws.cat, n, B(w->w_out), x, seg, mod, st, ws.qkv, ws.qkv_bytes, &ws);
   }
 }
 

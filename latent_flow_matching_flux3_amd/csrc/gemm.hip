@@ -81,6 +81,24 @@ int split_count(int m, int n, int k) {
 
 size_t split_bytes(int m, int n, int s) { return (size_t)s * ((m + 255) / 256) * 256 * n * 4; }
 
+// Stream-K on 256x256 tiles (gated residual): used where the whole tiles
+// leave part of the last round of workgroups idle and every run of K slices
+// is at least half a tile (so a tile has at most three parts), and the
+// longest workgroup's work shrinks by at least 5%: the output projection at
+// 4608 rows (216 tiles of 384 slices on 256 CUs: 324 slices per workgroup
+// against 384) or 4096 rows (192 tiles: 288 against 384).
+constexpr int kSkWaves = 4;                     // waves per workgroup (2 x 2)
+constexpr size_t kSkPartBytes = 128 * 128 * 4;  // one wave tile, fp32
+
+bool sk_plan(int m, int n, int k, long& tiles) {
+  if (m <= 0 || n % 256 != 0 || k % 32 != 0) return false;
+  tiles = (long)((m + 255) / 256) * (n / 256);
+  const long G = cu_count(), kt = k / 32, S = tiles * kt;
+  if (tiles % G == 0 || 2 * S < G * kt) return false;
+  const long rounds = (tiles + G - 1) / G;
+  return rounds * kt * G * 100 >= S * 105;
+}
+
 // Skinny products (M <= 128): the weight-streaming kernel, split over K when
 // its slabs alone (N / 128 workgroups) leave most CUs idle and the caller lent
 // scratch (gated residual and fp32 products).
@@ -193,6 +211,17 @@ void launch_gemm_fp8(const GemmArgs& g, hipStream_t st) {
   }
 }
 
+int gemm_sk_counters(int m, int n, int k) {
+  long tiles = 0;
+  return sk_plan(m, n, k, tiles) ? (int)tiles * kSkWaves : 0;
+}
+
+size_t gemm_sk_ws_bytes(int m, int n, int k) {
+  const int c = gemm_sk_counters(m, n, k);
+  if (c == 0) return 0;
+  return ((size_t)c * 4 + 255) / 256 * 256 + (size_t)cu_count() * 2 * kSkWaves * kSkPartBytes;
+}
+
 size_t gemm_split_ws_bytes(int m, int n, int k) {
   const int s = split_count(m, n, k);
   const size_t ring = s > 1 ? split_bytes(m, n, s) : 0;
@@ -279,6 +308,15 @@ void launch_gemm(const GemmArgs& g, hipStream_t st) {
       hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st,
                          (float*)g.C, g.ldc, (const float*)g.split_ws, stride, s, g.M, g.N,
                          gated ? g.mod : nullptr, g.mod_stride, g.gate_offset, g.seg);
+      return;
+    }
+  }
+  // Stream-K where whole tiles leave CUs idle in the last round.
+  if (gated && g.sk_cnt != nullptr) {
+    const size_t need = gemm_sk_ws_bytes(g.M, g.N, g.K);
+    if (need > 0 && need <= g.sk_bytes) {
+      hipLaunchKernelGGL((gemm::gemm_ring_kernel<256, 256, 2, 2, 32, 5, 1, GemmEpi::kGatedResidual, true>),
+                         dim3(cu_count()), dim3(256), 0, st, g, (g.M + 255) / 256, g.N / 256);
       return;
     }
   }

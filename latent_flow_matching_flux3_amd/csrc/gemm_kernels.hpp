@@ -28,6 +28,7 @@ namespace gemm {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gmem_void_t;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 
 
@@ -138,9 +139,19 @@ struct TileWalk {
 // SC (fp8 products): every value is first scaled by its row's and column's
 // scale, read from LDS (sc: the wave's 128 row scales, then at sc + 128 its
 // 128 column scales); LDS reads wait on lgkmcnt, not on the stores in flight.
-template <class T, GemmEpi EPI, bool SC = false>
+//
+// MG (stream-K, kGatedResidual): the tile's K range was split into two or
+// three parts; acc holds this wave's part, o1 and o2 the other parts' values
+// for the same wave tile (o2 null with two parts), in part order, stored by
+// sk_store_part.  They are added in part order whoever holds which part:
+// (P0 + P1) + P2, with own_last when acc is P2, else acc is P0 or P1 and
+// (acc + other) + P2 is the same sum exactly (IEEE addition commutes).
+template <class T, GemmEpi EPI, bool SC = false, bool MG = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::FM][T::FN],
-                                         int wrow0, int wcol0, const float* sc = nullptr) {
+                                         int wrow0, int wcol0, const float* sc = nullptr,
+                                         const float* o1 = nullptr, const float* o2 = nullptr,
+                                         bool own_last = false) {
+  static_assert(!MG || !SC, "stream-K merge: bf16 products");  // MG acts in the gated residual only
   int lane;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
   const int lr = lane & 31;
@@ -246,6 +257,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::F
     static_assert(EPI == GemmEpi::kGatedResidual, "epilogue kind");
     // x and gate are distinct buffers: all loads of one fragment are issued
     // before its stores.
+    constexpr int kSC1 = 16;  // buffer cache policy: bypass the non-coherent caches
+    constexpr int QB = T::FM * T::FN * 32 * 32 * 4;  // bytes of one wave tile's part
+    const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc((void*)o1, (short)0, QB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t r2 =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(o2 ? o2 : o1), (short)0, QB, 0x00020000);
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
       const int row = wrow0 + 32 * i + lr;
@@ -257,16 +273,33 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::F
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) {
           float4 gt[4], xv[4];
+          [[maybe_unused]] u32x4 p1[4], p2[4];
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int c = 32 * j + frag_col(g4, lane);
             gt[g4] = *(const float4*)(gate + c);
             xv[g4] = *(const float4*)(xrow + c);
+            if constexpr (MG) {
+              const int off = (((i * T::FN + j) * 4 + g4) * 64 + lane) * 16;
+              p1[g4] = __builtin_amdgcn_raw_buffer_load_b128(r1, off, 0, kSC1);
+              p2[g4] = o2 ? __builtin_amdgcn_raw_buffer_load_b128(r2, off, 0, kSC1) : u32x4{0, 0, 0, 0};
+            }
           }
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int c = 32 * j + frag_col(g4, lane);
-            const float4 f = f4(i, j, g4, sa);
+            float4 f = f4(i, j, g4, sa);
+            if constexpr (MG) {
+              const float4 a = make_float4(__uint_as_float(p1[g4][0]), __uint_as_float(p1[g4][1]),
+                                           __uint_as_float(p1[g4][2]), __uint_as_float(p1[g4][3]));
+              const float4 b = make_float4(__uint_as_float(p2[g4][0]), __uint_as_float(p2[g4][1]),
+                                           __uint_as_float(p2[g4][2]), __uint_as_float(p2[g4][3]));
+              if (own_last) {
+                f = make_float4((a.x + b.x) + f.x, (a.y + b.y) + f.y, (a.z + b.z) + f.z, (a.w + b.w) + f.w);
+              } else {
+                f = make_float4((f.x + a.x) + b.x, (f.y + a.y) + b.y, (f.z + a.z) + b.z, (f.w + a.w) + b.w);
+              }
+            }
             float4 r = xv[g4];
             r.x += gt[g4].x * f.x;
             r.y += gt[g4].y * f.y;
@@ -432,7 +465,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WAVES_PER_EU, GemmEpi EPI>
+//
+// SK (stream-K, kGatedResidual): the work is the product's K slices in tile
+// order (grouped order, KTT = K / BK slices per tile), cut into gridDim.x
+// equal runs; run v goes to the workgroup at position v of the XCD-major
+// order (the runs of one XCD are contiguous, so the parts of a tile mostly
+// share an L2).  A workgroup's items are the pieces of tiles its run covers
+// (the piece that starts inside a tile last, see `item`);
+// a tile covered by one run is finished as usual, a tile cut into parts
+// (two or three: runs are at least half a tile long) by the last of its
+// parts to arrive (sk_finish), with no workgroup ever waiting for another.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WAVES_PER_EU, GemmEpi EPI, bool SK = false>
 __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   using T = Tile<BM, BN, WM, WN>;
@@ -450,9 +493,18 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   static_assert(KSTEPS >= 2, "BK >= 32");
   __shared__ bf16x8 lds[STAGES * STAGE];
 
+  static_assert(!SK || EPI == GemmEpi::kGatedResidual, "stream-K: gated residual");
   const int splits = EPI == GemmEpi::kSplitPartial ? g.ksplit : 1;
-  const TileWalk walk(tiles_m * tiles_n * splits);
-  if (walk.count == 0) return;
+  const TileWalk walk(SK ? 0 : tiles_m * tiles_n * splits);
+  const int KTT = g.K / BK;  // K slices per tile
+  // Stream-K run [sk_s0, sk_s1) of the S slices; sk_t0 = its first tile.
+  const long sk_S = (long)tiles_m * tiles_n * KTT;
+  const int sk_v = SK && (gridDim.x & 7) == 0 ? (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3)
+                                              : blockIdx.x;
+  const long sk_s0 = (long)sk_v * sk_S / gridDim.x, sk_s1 = (long)(sk_v + 1) * sk_S / gridDim.x;
+  const int sk_t0 = (int)(sk_s0 / KTT);
+  const int count = SK ? (sk_s1 > sk_s0 ? (int)((sk_s1 - 1) / KTT) - sk_t0 + 1 : 0) : walk.count;
+  if (count == 0) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -474,12 +526,35 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   }
   const char* a_tile;
   const char* b_tile;
-  const int KT = g.K / BK / splits;  // K slices per work item, >= 1
+  const int KT = g.K / BK / splits;  // K slices per work item without SK, >= 1
+  // Stream-K work item i: tile `lin` of the grouped order, its K slices
+  // [kb, kb + len).  A run that starts inside a tile takes that piece last:
+  // every other item starts at k = 0, so the workgroups running at the same
+  // time stay within (tile length - run length) slices of the same k and
+  // share the A and B slices they read in L2 (taken in run order, the
+  // workgroups' k offsets would differ by multiples of the run length).
+  const int sk_rot = SK && count > 1 && sk_s0 % KTT != 0 ? 1 : 0;
+  auto item = [&](int i, int& lin, int& kb, int& len) {
+    lin = sk_t0 + (i + sk_rot) % count;
+    const long t0 = (long)lin * KTT;
+    kb = (int)(sk_s0 > t0 ? sk_s0 - t0 : 0);
+    len = (int)(sk_s1 - t0 < KTT ? sk_s1 - t0 : KTT) - kb;
+  };
+  int ld_len = KT;  // slices of the item the load cursor is in
   auto set_src = [&](int i) {
-    int tm, tn, split;
-    walk.coords(i, tiles_m, tiles_n, splits, tm, tn, split);
+    int tm, tn;
+    size_t k0;
+    if constexpr (SK) {
+      int lin, kb;
+      item(i, lin, kb, ld_len);
+      grouped_coords(lin, tiles_m, tiles_n, tm, tn);
+      k0 = (size_t)kb * BK;
+    } else {
+      int split;
+      walk.coords(i, tiles_m, tiles_n, splits, tm, tn, split);
+      k0 = (size_t)split * KT * BK;
+    }
     const int m0 = tm * BM;
-    const size_t k0 = (size_t)split * KT * BK;
     a_tile = (const char*)(g.A + (size_t)m0 * g.lda + k0);
     b_tile = (const char*)(g.B + (size_t)tn * BN * g.ldb + k0);
 #pragma unroll
@@ -520,13 +595,14 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   // slice is constant.
   int ld_i = 0, ld_kt = 0;
   auto advance_load = [&]() {
-    if (++ld_kt == KT) {
-      if (ld_i + 1 < walk.count) {
+    const int len = SK ? ld_len : KT;
+    if (++ld_kt == len) {
+      if (ld_i + 1 < count) {
         ++ld_i;
         ld_kt = 0;
         set_src(ld_i);
       } else {
-        ld_kt = KT - 1;
+        ld_kt = len - 1;
       }
     }
   };
@@ -602,14 +678,74 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   // Output origin of this wave in the tile being computed, found before the
   // tile's main loop (scalar registers), so nothing but the epilogue itself
   // runs between the last MFMA and the stores.
-  int out_row = 0, out_col = 0;
+  int out_row = 0, out_col = 0, cur_lin = 0, cur_kb = 0, cur_len = KT;
   auto set_out = [&](int i) {
-    int tm, tn, split;
-    walk.coords(i, tiles_m, tiles_n, splits, tm, tn, split);
+    int tm, tn, split = 0;
+    if constexpr (SK) {
+      item(i, cur_lin, cur_kb, cur_len);
+      grouped_coords(cur_lin, tiles_m, tiles_n, tm, tn);
+      cur_len = __builtin_amdgcn_readfirstlane(cur_len);
+    } else {
+      walk.coords(i, tiles_m, tiles_n, splits, tm, tn, split);
+    }
     out_row = __builtin_amdgcn_readfirstlane(split * tiles_m * BM + tm * BM + wm * T::WTM);
     out_col = __builtin_amdgcn_readfirstlane(tn * BN + wn * T::WTN);
   };
   auto store_tile = [&]() { epilogue<T, EPI>(g, acc, out_row, out_col); };
+  // Stream-K: the end of a part of a tile cut between runs.  Parts and runs:
+  // run v starts at slice floor(v S / G); the part of run v in this tile is
+  // that run's first item (slot side 0) or, if the run starts in an earlier
+  // tile, its last (side 1).  Each wave handles its own wave tile: unless the
+  // counter already shows every other part arrived, it stores its part
+  // (write-through stores, so another XCD's L2 cannot hold a stale copy),
+  // waits for the stores, and counts its arrival; the wave that completes the
+  // count (or found it complete) adds the parts in part order in the
+  // epilogue and resets the counter.  No wave ever waits for another.
+  auto sk_finish = [&]() {
+    const int G = gridDim.x;
+    auto run_of = [&](long s) { return (int)(((s + 1) * G + sk_S - 1) / sk_S - 1); };
+    auto side_of = [&](int v) { return ((long)v * sk_S / G) / KTT == cur_lin ? 0 : 1; };
+    constexpr int QF = T::WTM * T::WTN;
+    auto part = [&](int v) { return g.sk_part + (((size_t)v * 2 + side_of(v)) * NW + wave) * QF; };
+    const long t0 = (long)cur_lin * KTT;
+    const int v_first = run_of(t0);
+    const int parts = run_of(t0 + KTT - 1) - v_first + 1;
+    const int me = sk_v - v_first;
+    int* cnt = g.sk_cnt + (size_t)cur_lin * NW + wave;
+    int seen = 0;
+    if (lane == 0) seen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    seen = __builtin_amdgcn_readfirstlane(seen);
+    bool last = seen == parts - 1;
+    if (!last) {
+      constexpr int kSC1 = 16;
+      const __amdgpu_buffer_rsrc_t mine =
+          __builtin_amdgcn_make_buffer_rsrc((void*)part(sk_v), (short)0, QF * 4, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const u32x4 d = {__float_as_uint(acc[i][j][4 * g4]), __float_as_uint(acc[i][j][4 * g4 + 1]),
+                             __float_as_uint(acc[i][j][4 * g4 + 2]), __float_as_uint(acc[i][j][4 * g4 + 3])};
+            __builtin_amdgcn_raw_buffer_store_b128(d, mine, (((i * T::FN + j) * 4 + g4) * 64 + lane) * 16, 0, kSC1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      wait_vmcnt<0>();
+      int old = 0;
+      if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = __builtin_amdgcn_readfirstlane(old) == parts - 1;
+    }
+    if (last) {
+      const float* other[2] = {nullptr, nullptr};
+      int k = 0;
+      for (int p = 0; p < parts; ++p)
+        if (p != me) other[k++] = part(v_first + p);
+      epilogue<T, EPI, false, true>(g, acc, out_row, out_col, nullptr, other[0], other[1], me == 2);
+      if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
 
   // Prologue: slices 0 .. STAGES-2, then the refill of the last buffer is
   // opened as if at a barrier (its first LPS loads now, the rest in the
@@ -633,9 +769,9 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   read_frags(0, 0, 0);
 
   int slot = 0;
-  for (int ti = 0; ti < walk.count; ++ti) {
+  for (int ti = 0; ti < count; ++ti) {
     set_out(ti);
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = 0; kt < (SK ? cur_len : KT); ++kt) {
       // Steps 0 .. KSTEPS-2.  The fragments of a step were read a whole step
       // earlier; waiting for them before issuing the next reads keeps at most
       // FM + FN reads outstanding (lgkmcnt only counts to 15) and costs
@@ -661,7 +797,12 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
       step(PL{}, next * STAGE, 0, 0);
       slot = next;
     }
-    store_tile();
+    if constexpr (SK) {
+      if (cur_kb == 0 && cur_len == KTT) store_tile();
+      else sk_finish();
+    } else {
+      store_tile();
+    }
     zero_acc();
     __builtin_amdgcn_sched_barrier(0);
     // First fragments of the next tile (after the last tile: unused).

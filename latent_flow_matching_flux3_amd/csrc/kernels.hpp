@@ -64,11 +64,26 @@ struct GemmArgs {
   const float* w_scale0;
   const float* a_ratio;
   const float* w_ratio;
+  // kGatedResidual on 256x256 tiles: optional stream-K scratch (gemm_sk_ws_bytes,
+  // carved by gemm_sk_carve).  Every workgroup then takes an equal run of the
+  // product's K slices in tile order, and a tile split between workgroups is
+  // finished by the last of its parts to arrive.  sk_cnt: one arrival counter
+  // per (tile, wave), zero before a launch and zero again after it; sk_part:
+  // the parts' fp32 partial products.  Null: whole tiles per workgroup.
+  int* sk_cnt;
+  float* sk_part;
+  size_t sk_bytes;
 };
 
 // Scratch bytes a kGatedResidual or kStoreF32 product of this shape uses when
 // split over K (0: it is not split).
 size_t gemm_split_ws_bytes(int m, int n, int k);
+// Stream-K scratch of a kGatedResidual product of this shape on this device:
+// 0 where the whole tiles already fill the CUs evenly (or too few tiles for
+// a split), else counters (gemm_sk_counters of them, first) and partial
+// slots.  The counters must be zero before the first launch.
+size_t gemm_sk_ws_bytes(int m, int n, int k);
+int gemm_sk_counters(int m, int n, int k);
 
 // fp8 (E4M3, rowwise-scaled) products: shapes the kernel takes, and launch.
 bool gemm_fp8_shape_ok(int m, int n, int k);
