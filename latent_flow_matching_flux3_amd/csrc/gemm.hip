@@ -105,11 +105,11 @@ bool sk_plan(int m, int n, int k, long& tiles) {
 bool skinny_shape(int m, int n, int k) { return m > 0 && m <= 128 && n % 128 == 0 && k % 64 == 0; }
 
 int skinny_split(int n, int k) {
+  // K ranges need not divide K / 64 evenly (the kernel splits it as evenly as
+  // it goes), so the split fills the CUs: the output projection at <= 128 rows
+  // (24 slabs) takes 10 ranges of 19 or 20 slices instead of 8 of 24.
   const int slabs = n / 128, kt = k / 64;
-  int best = 1;
-  for (int d = 2; d <= 16 && kt / d >= 4; ++d)
-    if (kt % d == 0 && (long)slabs * d <= cu_count()) best = d;
-  return best;
+  return std::max(1, std::min({16, cu_count() / slabs, kt / 4}));
 }
 
 size_t skinny_split_bytes(int m, int n, int d) { return (size_t)d * ((m + 31) / 32) * 32 * n * 4; }
@@ -236,7 +236,7 @@ template <int MT, GemmEpi EPI>
 void launch_skinny(const GemmArgs& g, int ksplit, hipStream_t st) {
   const int slabs = g.N / 128;
   hipLaunchKernelGGL((gemm::gemm_skinny_kernel<MT, EPI>), dim3(slabs * ksplit), dim3(256), 0, st, g,
-                     slabs, g.K / 64 / ksplit);
+                     slabs, ksplit);
 }
 
 template <int MT>

@@ -836,7 +836,7 @@ struct SkinnyTile {
 };
 
 template <int MT, GemmEpi EPI>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g, int slabs, int kt_per) {
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g, int slabs, int ksplit) {
   using T = SkinnyTile<MT>;
   using Lay = Layout<64>;
   constexpr int CPR = Lay::CPR;            // 8 chunks of 16 bytes per row
@@ -857,7 +857,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g, int slabs,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wk = wave >> 1;
   const int n0 = slab * BN;
-  const size_t k0 = (size_t)split * kt_per * 64;
+  // K range of this split: slices [kt0, kt0 + kt_per) of 64, the K / 64
+  // slices cut as evenly as they go (ranges differ by at most one slice).
+  const int kt_all = g.K / 64;
+  const int kt0 = split * kt_all / ksplit;
+  const int kt_per = (split + 1) * kt_all / ksplit - kt0;
+  const size_t k0 = (size_t)kt0 * 64;
 
   // Block b of a slice: X rows 8b .. 8b+7 (b < X_BLK), else W rows; lane t
   // lands at row t/8, physical chunk t%8 of the block, so it fetches the

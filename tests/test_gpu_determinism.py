@@ -75,7 +75,10 @@ def test_block_and_kernels_twice(L, fp8):
 
     _equal(*_twice(ln), "ln_modulate")
     qkv = torch.empty((n, 9216), dtype=torch.bfloat16, device="cuda")
+    # the o part of [o | h] gets seeded values (the in-projection writes h):
+    # left uninitialised it may hold NaN patterns, which compare unequal
     cat = torch.empty((n, 12288), dtype=torch.bfloat16, device="cuda")
+    cat[:, :3072] = dev(syn.normal_bf16((n, 3072), 1.0, 66, "det.o"))
 
     def in_proj():
         L.flux3_block_in_proj(xm, blk.w_in, qkv, cat[:, 3072:])
