@@ -37,11 +37,11 @@ COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
 # its 4608-row launches inside stack steps (as its roofline is timed); the
 # others are of their kernel alone (--only).
 TRAFFIC = {
-    "gemm_in_proj_swiglu": (1441.2e6 + 169.9e6, {"gemm_kernels.hpp": "e23fadde033345f2", "gemm.hip": "686b4c2d632847e7",
-                                                 "kernels.hpp": "0548d5d1c5b3415e", "common.hpp": "a628a66ce9fdd5dc"}),
-    "gemm_out_proj_gated": (746.8e6 + 59.3e6, {"gemm_kernels.hpp": "e23fadde033345f2", "gemm.hip": "686b4c2d632847e7",
-                                               "kernels.hpp": "0548d5d1c5b3415e", "common.hpp": "a628a66ce9fdd5dc"}),
-    "attention": (356.9e6 + 89.9e6, {"attention.hip": "bbd9a581ae964ab5", "kernels.hpp": "0548d5d1c5b3415e", "common.hpp": "a628a66ce9fdd5dc"}),
+    "gemm_in_proj_swiglu": (1446.9e6 + 169.9e6, {"gemm_kernels.hpp": "e23ac2e9a0eb236b", "gemm.hip": "ead7b079a9d71a48",
+                                                 "kernels.hpp": "bdc51f72978b844d", "common.hpp": "a628a66ce9fdd5dc"}),
+    "gemm_out_proj_gated": (748.4e6 + 59.3e6, {"gemm_kernels.hpp": "e23ac2e9a0eb236b", "gemm.hip": "ead7b079a9d71a48",
+                                               "kernels.hpp": "bdc51f72978b844d", "common.hpp": "a628a66ce9fdd5dc"}),
+    "attention": (356.5e6 + 90.3e6, {"attention.hip": "bbd9a581ae964ab5", "kernels.hpp": "bdc51f72978b844d", "common.hpp": "a628a66ce9fdd5dc"}),
 }
 
 

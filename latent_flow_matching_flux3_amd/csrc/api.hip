@@ -193,8 +193,10 @@ class TimedLaunch {
   hipStream_t st_ = nullptr;
 };
 
-// a4 + a5: [q | k | v] and h_mlp = silu(a) * b in one product over w_in.
-void in_proj(const bf16* xm, int n, const bf16* w_in, bf16* qkv, bf16* h, int ldh, hipStream_t st) {
+// a4 + a5: [q | k | v] and h_mlp = silu(a) * b in one product over w_in;
+// with q_scale (skinny products only), also a6 on q and k in the epilogue.
+void in_proj(const bf16* xm, int n, const bf16* w_in, bf16* qkv, bf16* h, int ldh, hipStream_t st,
+             const bf16* q_scale = nullptr, const bf16* k_scale = nullptr, const float* table = nullptr) {
   GemmArgs g{};
   g.A = xm;
   g.lda = kHidden;
@@ -208,13 +210,16 @@ void in_proj(const bf16* xm, int n, const bf16* w_in, bf16* qkv, bf16* h, int ld
   g.ldc = 3 * kHidden;
   g.H = h;
   g.ldh = ldh;
+  g.qk_scale_q = q_scale;
+  g.qk_scale_k = k_scale;
+  g.rope_table = q_scale ? table : nullptr;
   launch_gemm(g, st);
 }
 
 // a8: x += gate * ([o | h] [W_o | W_out]^T).
 void out_proj(const bf16* cat, int n, const bf16* w_out, float* x, const SegTable& seg,
               const float* mod, hipStream_t st, void* scratch = nullptr, size_t scratch_bytes = 0,
-              const BlockWs* ws = nullptr) {
+              const BlockWs* ws = nullptr, bf16* ln_out = nullptr) {
   GemmArgs o{};
   o.A = cat;
   o.lda = kWOutCols;
@@ -237,16 +242,24 @@ void out_proj(const bf16* cat, int n, const bf16* w_out, float* x, const SegTabl
     o.sk_part = ws->sk_part;
     o.sk_bytes = ws->sk_bytes;
   }
+  o.ln_out = ln_out;
+  o.ln_ldo = kHidden;
   launch_gemm(o, st);
 }
 
 // a3..a8 with arguments already checked.
 // attn: row groups that attend only within themselves (the samples of a
 // pack, or two text streams in stage 1); nullptr = all n rows together.
-void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* mod,
+// ln_ready: ws.xm already holds a3 of x (the previous block's output
+// projection wrote it).  next_ln: the next block uses the same workspace,
+// rows, segments and mod, so this block may write its a3 into ws.xm.
+// Returns whether it did (then the next block is called with ln_ready).
+bool block_forward_unchecked(float* x, int n, const SegTable& seg, const float* mod,
                              const flux3_block_weights* w, const float* table, const BlockWs& ws,
-                             hipStream_t st, const SegTable* attn = nullptr) {
+                             hipStream_t st, const SegTable* attn = nullptr, bool ln_ready = false,
+                             bool next_ln = false) {
   const bool fp8 = w->w_in_fp8 != nullptr;
+  const bool fuse_qk = !fp8 && ws.nzero == 0 && gemm_skinny_used(n, kWInRows, kHidden);
   uint8_t* const xm8 = (uint8_t*)ws.xm;
   if (fp8) {
     // a3 with the rowwise FP8 quantization fused; a4 + a5 as an fp8r product
@@ -273,16 +286,22 @@ void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
     launch_gemm_fp8(g, st);
   } else {
     // a3: h = (1 + scale) LN(x) + shift
-    {
+    if (!ln_ready) {
       TimedLaunch t(FLUX3_TIMER_LN_MODULATE, n, st);
       launch_ln_modulate(x, kHidden, ws.xm, kHidden, n, seg, mod, 3 * kHidden, st);
     }
-    // a4 + a5: q | k | v into qkv; SwiGLU output into the last 9216 columns of cat
+    // a4 + a5: q | k | v into qkv; SwiGLU output into the last 9216 columns of
+    // cat.  Products of at most 128 rows run on the skinny kernel, which also
+    // applies a6 (when no counters are waiting for the norm kernel to clear them).
     TimedLaunch t(FLUX3_TIMER_IN_PROJ, n, st);
-    in_proj(ws.xm, n, B(w->w_in), ws.qkv, ws.cat + kHidden, kWOutCols, st);
+    if (fuse_qk)
+      in_proj(ws.xm, n, B(w->w_in), ws.qkv, ws.cat + kHidden, kWOutCols, st, B(w->q_scale), B(w->k_scale),
+              table);
+    else
+      in_proj(ws.xm, n, B(w->w_in), ws.qkv, ws.cat + kHidden, kWOutCols, st);
   }
   // a6: RMSNorm + RoPE on q and k
-  {
+  if (!fuse_qk) {
     TimedLaunch t(FLUX3_TIMER_QK_NORM_ROPE, n, st);
     launch_qk_norm_rope(ws.qkv, 3 * kHidden, ws.qkv + kHidden, 3 * kHidden, n, B(w->q_scale),
                         B(w->k_scale), table, st, ws.zero, ws.nzero);
@@ -332,9 +351,14 @@ void block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
     TimedLaunch t(FLUX3_TIMER_OUT_PROJ, n, st);
     launch_gemm_fp8(o, st);
   } else {
+    // products of at most 128 rows split over K: the reduce also writes the
+    // next block's a3 (xm is dead once the input projection has run)
+    const bool ln_next = next_ln && gemm_fuses_next_ln(n, kHidden, kWOutCols, ws.qkv_bytes);
     TimedLaunch t(FLUX3_TIMER_OUT_PROJ, n, st);
-    out_proj(ws.cat, n, B(w->w_out), x, seg, mod, st, ws.qkv, ws.qkv_bytes, &ws);
+    out_proj(ws.cat, n, B(w->w_out), x, seg, mod, st, ws.qkv, ws.qkv_bytes, &ws, ln_next ? ws.xm : nullptr);
+    return ln_next;
   }
+  return false;
 }
 
 }  // namespace
@@ -1009,11 +1033,12 @@ int stack_forward_unchecked(const flux3_model_weights* w, const uint16_t* img, i
     seg.off[0] = 0;
     seg.off[1] = counts[i];
     seg.n = 1;
+    bool ln = false;  // a3 of the next block already in the workspace
     for (int b = 0; b < w->n_early; ++b)
-      block_forward_unchecked(s.x + (size_t)row0[i] * kHidden, counts[i], seg,
-                              s.mod_early + (size_t)i * 3 * kHidden, &w->early[m][b],
-                              table + (size_t)row0[i] * 128, beside ? sws : bws,
-                              beside ? side->s : stream);
+      ln = block_forward_unchecked(s.x + (size_t)row0[i] * kHidden, counts[i], seg,
+                                   s.mod_early + (size_t)i * 3 * kHidden, &w->early[m][b],
+                                   table + (size_t)row0[i] * 128, beside ? sws : bws,
+                                   beside ? side->s : stream, nullptr, ln, b + 1 < w->n_early);
   }
   if (side != nullptr) {
     rc = side_join(side, stream);
@@ -1025,8 +1050,10 @@ int stack_forward_unchecked(const flux3_model_weights* w, const uint16_t* img, i
   for (int i = 0; i < n_modes; ++i) seg.off[i] = row0[i];
   seg.off[n_modes] = n_total;
   seg.n = n_modes;
+  bool ln = false;
   for (int b = 0; b < w->n_single; ++b)
-    block_forward_unchecked(s.x, n_total, seg, s.mod_single, &w->single[b], table, bws, stream);
+    ln = block_forward_unchecked(s.x, n_total, seg, s.mod_single, &w->single[b], table, bws, stream, nullptr,
+                                 ln, b + 1 < w->n_single);
 
   // a12: final layer on the image rows.
   SegTable one{};
@@ -1358,16 +1385,19 @@ int stack_cfg_unchecked(const flux3_model_weights* w, const uint16_t* img, const
   int mi = 0;
   {
     one.off[1] = r.n_img;
+    bool ln = false;
     for (int b = 0; b < w->n_early; ++b)
-      block_forward_unchecked(s.x, r.n_img, one, s.mod_early, &w->early[0][b], table, bws, stream);
+      ln = block_forward_unchecked(s.x, r.n_img, one, s.mod_early, &w->early[0][b], table, bws, stream, nullptr,
+                                   ln, b + 1 < w->n_early);
     ++mi;
   }
   if (r.n_cond > 0) {
     one.off[1] = r.n_cond;
+    bool ln = false;
     for (int b = 0; b < w->n_early; ++b)
-      block_forward_unchecked(s.x + (size_t)r.n_img * kHidden, r.n_cond, one,
-                              s.mod_early + (size_t)mi * 3 * kHidden, &w->early[1][b],
-                              table + (size_t)r.n_img * 128, sws, s1);
+      ln = block_forward_unchecked(s.x + (size_t)r.n_img * kHidden, r.n_cond, one,
+                                   s.mod_early + (size_t)mi * 3 * kHidden, &w->early[1][b],
+                                   table + (size_t)r.n_img * 128, sws, s1, nullptr, ln, b + 1 < w->n_early);
     ++mi;
   }
   if (nt > 0) {
@@ -1377,10 +1407,11 @@ int stack_cfg_unchecked(const flux3_model_weights* w, const uint16_t* img, const
     groups.off[1] = r.n_t0;
     groups.off[2] = nt;
     groups.n = 2;
+    bool ln = false;
     for (int b = 0; b < w->n_early; ++b)
-      block_forward_unchecked(s.x + (size_t)r.txt0() * kHidden, nt, one,
-                              s.mod_early + (size_t)mi * 3 * kHidden, &w->early[2][b],
-                              table + (size_t)r.txt0() * 128, sws, s1, &groups);
+      ln = block_forward_unchecked(s.x + (size_t)r.txt0() * kHidden, nt, one,
+                                   s.mod_early + (size_t)mi * 3 * kHidden, &w->early[2][b],
+                                   table + (size_t)r.txt0() * 128, sws, s1, &groups, ln, b + 1 < w->n_early);
   }
   if (side != nullptr) {
     rc = side_join(side, stream);
@@ -1399,8 +1430,10 @@ int stack_cfg_unchecked(const flux3_model_weights* w, const uint16_t* img, const
   samples.off[1] = r.n0();
   samples.off[2] = n;
   samples.n = 2;
+  bool ln = false;
   for (int b = 0; b < w->n_single; ++b)
-    block_forward_unchecked(s.x, n, seg2, s.mod_seg, &w->single[b], table, bws, stream, &samples);
+    ln = block_forward_unchecked(s.x, n, seg2, s.mod_seg, &w->single[b], table, bws, stream, &samples, ln,
+                                 b + 1 < w->n_single);
 
   // a12: final layer on both samples' image rows, then guidance.
   one.off[1] = r.n_img;

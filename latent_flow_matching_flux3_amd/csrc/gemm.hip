@@ -65,16 +65,20 @@ void run_ring(const GemmArgs& g, hipStream_t st) {
   }
 }
 
+// Most K ranges a split product takes (the reduce holds one load per range
+// in flight).
+constexpr int kMaxReduceSplits = 24;
+
 // K ranges for a split product on 256x256 tiles: the largest
-// divisor s of K/32 with s * tiles <= CUs and ranges of at least 16 slices of
-// 32; 1 when the product already has 128 tiles or more.
+// divisor s of K/32 with s * tiles <= CUs, s <= kMaxReduceSplits and ranges of
+// at least 16 slices of 32; 1 when the product already has 128 tiles or more.
 int split_count(int m, int n, int k) {
   if (n % 256 != 0 || k % 32 != 0) return 1;
   const long tiles = (long)((m + 255) / 256) * (n / 256);
   if (tiles >= 128) return 1;
   const int kt = k / 32;
   int best = 1;
-  for (int s = 2; s <= kt / 16; ++s)
+  for (int s = 2; s <= kt / 16 && s <= kMaxReduceSplits; ++s)
     if (kt % s == 0 && tiles * s <= cu_count()) best = s;
   return best;
 }
@@ -125,14 +129,20 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(float* x, int ldx, co
   if (idx >= (size_t)m * quads) return;
   const int r = (int)(idx / quads), c = (int)(idx % quads) * 4;
   const float* p = part + (size_t)r * n + c;
-  float4 acc = *(const float4*)p;
-  for (int sp = 1; sp < splits; ++sp) {
-    const float4 t = *(const float4*)(p + sp * stride);
-    acc.x += t.x;
-    acc.y += t.y;
-    acc.z += t.z;
-    acc.w += t.w;
-  }
+  // every partial's load in flight at once, then the sum in split order
+  float4 t[kMaxReduceSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxReduceSplits; ++sp)
+    if (sp < splits) t[sp] = *(const float4*)(p + sp * stride);
+  float4 acc = t[0];
+#pragma unroll
+  for (int sp = 1; sp < kMaxReduceSplits; ++sp)
+    if (sp < splits) {
+      acc.x += t[sp].x;
+      acc.y += t[sp].y;
+      acc.z += t[sp].z;
+      acc.w += t[sp].w;
+    }
   float4* xp = (float4*)(x + (size_t)r * ldx + c);
   if (mod == nullptr) {
     *xp = acc;
@@ -145,6 +155,88 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(float* x, int ldx, co
   xv.z += gt.z * acc.z;
   xv.w += gt.w * acc.w;
   *xp = xv;
+}
+
+// The reduce of a skinny split product (N = 3072) with the next block's
+// LayerNorm + modulation: one workgroup per row, thread t owns columns
+// 4 (t + 256 i), i < 3.  The sum of the partials and the gated residual are
+// those of split_reduce_kernel; the LayerNorm is the exact two-pass form of
+// ln_modulate_kernel (mean, then mean((x - mu)^2), eps 1e-6, in fp32), its
+// row sums formed per wave and then over the four waves.
+__global__ __launch_bounds__(256) void split_reduce_ln_kernel(float* x, int ldx, const float* part,
+                                                              size_t stride, int splits,
+                                                              const float* mod, int mod_stride,
+                                                              int gate_offset, SegTable seg, bf16* xm,
+                                                              int ldxm) {
+  __shared__ float red[2][4];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* shift = mod + (size_t)seg_of_row(seg, row) * mod_stride;
+  float v[3][4];
+  float s = 0.f;
+  // every partial's load in flight at once (splits <= 16 on this path), then
+  // the sums in split order
+  float4 t[3][16];
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+#pragma unroll
+    for (int sp = 0; sp < 16; ++sp)
+      if (sp < splits) t[i][sp] = *(const float4*)(part + (size_t)row * kHidden + (tid + 256 * i) * 4 + sp * stride);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int c = (tid + 256 * i) * 4;
+    float4 acc = t[i][0];
+#pragma unroll
+    for (int sp = 1; sp < 16; ++sp)
+      if (sp < splits) {
+        acc.x += t[i][sp].x;
+        acc.y += t[i][sp].y;
+        acc.z += t[i][sp].z;
+        acc.w += t[i][sp].w;
+      }
+    const float4 gt = *(const float4*)(shift + gate_offset + c);
+    float4* xp = (float4*)(x + (size_t)row * ldx + c);
+    float4 xv = *xp;
+    xv.x += gt.x * acc.x;
+    xv.y += gt.y * acc.y;
+    xv.z += gt.z * acc.z;
+    xv.w += gt.w * acc.w;
+    *xp = xv;
+    v[i][0] = xv.x;
+    v[i][1] = xv.y;
+    v[i][2] = xv.z;
+    v[i][3] = xv.w;
+    s += (xv.x + xv.y) + (xv.z + xv.w);
+  }
+  s = wave_sum(s);
+  if (lane == 0) red[0][wave] = s;
+  __syncthreads();
+  const float mu = ((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) * (1.0f / kHidden);
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float d = v[i][e] - mu;
+      q += d * d;
+    }
+  q = wave_sum(q);
+  if (lane == 0) red[1][wave] = q;
+  __syncthreads();
+  const float var = ((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) * (1.0f / kHidden);
+  const float rstd = 1.0f / sqrtf(var + 1e-6f);
+  const float* scale = shift + kHidden;
+  bf16* orow = xm + (size_t)row * ldxm;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int c = (tid + 256 * i) * 4;
+    const float4 sh = *(const float4*)(shift + c), sc = *(const float4*)(scale + c);
+    bf16x4 o;
+    o[0] = to_bf16((1.0f + sc.x) * ((v[i][0] - mu) * rstd) + sh.x);
+    o[1] = to_bf16((1.0f + sc.y) * ((v[i][1] - mu) * rstd) + sh.y);
+    o[2] = to_bf16((1.0f + sc.z) * ((v[i][2] - mu) * rstd) + sh.z);
+    o[3] = to_bf16((1.0f + sc.w) * ((v[i][3] - mu) * rstd) + sh.w);
+    *(bf16x4*)(orow + c) = o;
+  }
 }
 
 // fp8 products: the persistent ring kernel with 4 slices of 64 fp8 in flight.
@@ -161,7 +253,8 @@ void launch_ring_fp8(const GemmArgs& g, hipStream_t st) {
 }
 
 // K ranges of a split fp8 product: the largest divisor s of K/128 with
-// s * tiles <= CUs and ranges of at least two 128-wide units (the ring needs
+// s * tiles <= CUs, s <= kMaxReduceSplits and ranges of at least two
+// 128-wide units (the ring needs
 // an even number of slices, at least as many as its stages); 1 when the
 // product already has 128 tiles or more.
 int split_count_fp8(int m, int n, int k) {
@@ -169,7 +262,7 @@ int split_count_fp8(int m, int n, int k) {
   if (tiles >= 128) return 1;
   const int ku = k / 128;
   int best = 1;
-  for (int s = 2; s <= ku / 2; ++s)
+  for (int s = 2; s <= ku / 2 && s <= kMaxReduceSplits; ++s)
     if (ku % s == 0 && tiles * s <= cu_count()) best = s;
   return best;
 }
@@ -211,6 +304,14 @@ void launch_gemm_fp8(const GemmArgs& g, hipStream_t st) {
   }
 }
 
+bool gemm_skinny_used(int m, int n, int k) { return skinny_shape(m, n, k); }
+
+bool gemm_fuses_next_ln(int m, int n, int k, size_t scratch_bytes) {
+  if (!skinny_shape(m, n, k) || n != kHidden) return false;
+  const int d = skinny_split(n, k);
+  return d > 1 && skinny_split_bytes(m, n, d) <= scratch_bytes;
+}
+
 int gemm_sk_counters(int m, int n, int k) {
   long tiles = 0;
   return sk_plan(m, n, k, tiles) ? (int)tiles * kSkWaves : 0;
@@ -250,6 +351,12 @@ void run_skinny_mt(const GemmArgs& g, hipStream_t st) {
       h.C = g.split_ws;
       h.ldc = g.N;
       launch_skinny<MT, GemmEpi::kSplitPartial>(h, d, st);
+      if (gated && g.ln_out != nullptr && g.N == kHidden) {
+        hipLaunchKernelGGL(split_reduce_ln_kernel, dim3(g.M), dim3(256), 0, st, (float*)g.C, g.ldc,
+                           (const float*)g.split_ws, (size_t)32 * MT * g.N, d, g.mod, g.mod_stride,
+                           g.gate_offset, g.seg, g.ln_out, g.ln_ldo);
+        return;
+      }
       const size_t quads = (size_t)g.M * (g.N / 4);
       hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st,
                          (float*)g.C, g.ldc, (const float*)g.split_ws, (size_t)32 * MT * g.N, d, g.M,

@@ -835,6 +835,82 @@ struct SkinnyTile {
   static constexpr int FM = MT, FN = 2;
 };
 
+// Epilogue of a q or k slab of the skinny in-projection with the head's
+// RMSNorm and RoPE (the arithmetic of qk_norm_rope_kernel: the projection
+// rounded to bf16, then x / sqrt(mean_128(x^2) + 1e-6) * scale, then each
+// pair (2p, 2p+1) rotated by the token's table entry p, rounded to bf16).
+// Wave (wn, 0) holds head columns 64 wn .. 64 wn + 63 of rows 32 i + lane % 32
+// (four consecutive columns per register group, lane halves interleaved by
+// four); its row sums of squares go to ss[wn][row] for the other wave.  All
+// four waves call this (it holds a barrier); only wk == 0 stores.
+template <int MT>
+__device__ __forceinline__ void skinny_qk_norm_rope(const GemmArgs& g, floatx16 (&acc)[MT][2], int n0, int wn,
+                                                    int wk, int lane, float* ss) {
+  const int lr = lane & 31;
+  const bool is_k = n0 >= kHidden;
+  float part[MT];
+  bf16x4 sc[2][4];
+  float4 tb[MT][2][4];
+  if (wk == 0) {
+    // the scales of this lane's columns and the rotations of its rows (rows
+    // past M-1 read row M-1's), loaded before the exchange so their latency
+    // overlaps it
+    const bf16* scale = (is_k ? g.qk_scale_k : g.qk_scale_q) + wn * 64;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) sc[j][g4] = *(const bf16x4*)(scale + 32 * j + frag_col(g4, lane));
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const float* t = g.rope_table + (size_t)min(32 * i + lr, g.M - 1) * 128 + wn * 64;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) tb[i][j][g4] = *(const float4*)(t + 32 * j + frag_col(g4, lane));
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v = to_f32(to_bf16(acc[i][j][r]));
+          s += v * v;
+        }
+      part[i] = s + __shfl_xor(s, 32, 64);
+      if (lane < 32) ss[wn * 32 * MT + 32 * i + lr] = part[i];
+    }
+  }
+  __syncthreads();
+  if (wk != 0) return;
+  bf16* C = (bf16*)g.C;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int row = 32 * i + lr;
+    if (row >= g.M) continue;
+    const float tot = part[i] + ss[(wn ^ 1) * 32 * MT + 32 * i + lr];
+    const float rn = 1.0f / sqrtf(tot * (1.0f / kHeadDim) + 1e-6f);
+    bf16* crow = C + (size_t)row * g.ldc + n0 + wn * 64;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int c = 32 * j + frag_col(g4, lane);  // column within this wave's 64
+        const float4 t = tb[i][j][g4];              // (cos, sin) of pairs c/2, c/2 + 1
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = to_f32(to_bf16(acc[i][j][4 * g4 + e])) * rn * to_f32(sc[j][g4][e]);
+        bf16x4 o;
+        o[0] = to_bf16(v[0] * t.x - v[1] * t.y);
+        o[1] = to_bf16(v[0] * t.y + v[1] * t.x);
+        o[2] = to_bf16(v[2] * t.z - v[3] * t.w);
+        o[3] = to_bf16(v[2] * t.w + v[3] * t.z);
+        *(bf16x4*)(crow + c) = o;
+      }
+  }
+}
+
 template <int MT, GemmEpi EPI>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g, int slabs, int ksplit) {
   using T = SkinnyTile<MT>;
@@ -849,7 +925,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g, int slabs,
   static_assert(BLK % 4 == 0, "a slice's blocks split evenly over the 4 waves");
   constexpr int PER = BLK / 4;             // loads per wave per slice
   static_assert((STAGES - 1) * PER < 64, "vmcnt range");
-  static_assert(2 * MT * 2 * 16 * 64 * 4 <= STAGES * STAGE * 16, "K-half reduction fits the ring");
+  static_assert(2 * MT * 2 * 16 * 64 * 4 + 2 * MP * 4 <= STAGES * STAGE * 16,
+                "K-half reduction and the QK norm's row sums fit the ring");
   __shared__ bf16x8 lds[STAGES * STAGE];
 
   const int slab = blockIdx.x % slabs, split = blockIdx.x / slabs;
@@ -947,6 +1024,17 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g, int slabs,
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * 2 + j) * 16 + r) * 64 + lane];
+  }
+  // A slab of the q or k columns is one head: its two epilogue waves (64
+  // columns each) exchange each row's sum of squares through LDS, then store
+  // the head normalised and rotated (workgroup-uniform branch).
+  if constexpr (EPI == GemmEpi::kInProj) {
+    if (g.rope_table != nullptr && n0 < 2 * kHidden) {
+      skinny_qk_norm_rope<MT>(g, acc, n0, wn, wk, lane, (float*)lds + 2 * (MT * 2 * 16 * 64));
+      return;
+    }
+  }
+  if (wk == 0) {
     const int wrow0 = EPI == GemmEpi::kSplitPartial ? split * MP : 0;
     epilogue<T, EPI>(g, acc, wrow0, n0 + wn * 64);
   }

@@ -73,6 +73,19 @@ struct GemmArgs {
   int* sk_cnt;
   float* sk_part;
   size_t sk_bytes;
+  // kInProj on the skinny kernel (M <= 128): optional QK RMSNorm + RoPE in
+  // the epilogue (q_scale / k_scale bf16 [128], rope_table [M][64][2] as for
+  // launch_qk_norm_rope): the q and k columns are stored normalised and
+  // rotated, so no separate norm kernel runs.  Null: plain q | k | v stores.
+  const bf16* qk_scale_q;
+  const bf16* qk_scale_k;
+  const float* rope_table;
+  // kGatedResidual on the skinny kernel split over K: optional output of the
+  // next block's LayerNorm + modulation of the updated rows (same mod and
+  // segments: shift at mod + s * mod_stride, scale 3072 further), bf16 with
+  // row stride ln_ldo, written by the reduce (gemm_fuses_next_ln tells when).
+  bf16* ln_out;
+  int ln_ldo;
 };
 
 // Scratch bytes a kGatedResidual or kStoreF32 product of this shape uses when
@@ -83,6 +96,13 @@ size_t gemm_split_ws_bytes(int m, int n, int k);
 // a split), else counters (gemm_sk_counters of them, first) and partial
 // slots.  The counters must be zero before the first launch.
 size_t gemm_sk_ws_bytes(int m, int n, int k);
+// True where launch_gemm runs the skinny kernel (M <= 128 rows), whose
+// in-projection epilogue can apply the QK norm (GemmArgs::rope_table).
+bool gemm_skinny_used(int m, int n, int k);
+// True where a kGatedResidual product of this shape, lent `scratch_bytes` of
+// split scratch, runs split over K on the skinny kernel and so applies
+// GemmArgs::ln_out in its reduce.
+bool gemm_fuses_next_ln(int m, int n, int k, size_t scratch_bytes);
 int gemm_sk_counters(int m, int n, int k);
 
 // fp8 (E4M3, rowwise-scaled) products: shapes the kernel takes, and launch.

@@ -300,8 +300,12 @@ def _run_block(L, ids, segs, w, x, mods):
     return xd
 
 
+# 1, 33, 55, 96 and 128 rows run the skinny in-projection with the QK norm
+# in its epilogue (one to four 32-row fragments, ragged), 600 rows the ring
+# kernel and the norm kernel.
 @pytest.mark.parametrize("lay", [syn.Layout(8, 8, 32), syn.Layout(5, 6, 13, [(3, 4)]),
-                                 syn.Layout(16, 20, 88, [(8, 24)])])
+                                 syn.Layout(16, 20, 88, [(8, 24)]), syn.Layout(1, 1, 0),
+                                 syn.Layout(4, 4, 17), syn.Layout(8, 12, 32)])
 def test_block_forward(L, lay):
     ids, segs, w, x, mods = _block_inputs(61, lay)
     say(f"block_forward n={len(ids)}")

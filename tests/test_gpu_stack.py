@@ -476,11 +476,14 @@ def test_launch_timer(L):
     recs = L.flux3_timer_stop(64)
     assert torch.equal(v, plain), "the timer changed the result"
     order = ["ln_modulate", "in_proj", "qk_norm_rope", "attention", "out_proj"]
+    # at most 128 rows the in-projection applies the QK norm itself
+    fused = [k for k in order if k != "qk_norm_rope"]
     # stage 1: the image block (96 rows) and the text block (40 rows, side
     # stream); stage 2: two joint blocks (136 rows)
-    assert sorted((k, r) for k, r, _ in recs) == sorted((k, r) for r in (96, 40, 136, 136) for k in order)
-    assert [k for k, r, _ in recs if r != 40] == order * 3
-    assert [k for k, r, _ in recs if r == 40] == order
+    expect = [(k, r) for r in (96, 40) for k in fused] + [(k, 136) for _ in range(2) for k in order]
+    assert sorted((k, r) for k, r, _ in recs) == sorted(expect)
+    assert [k for k, r, _ in recs if r != 40] == fused + order * 2
+    assert [k for k, r, _ in recs if r == 40] == fused
     assert all(ms > 0 for _, _, ms in recs)
     say("launch timer: capacity")
     L.flux3_timer_start(["in_proj", "attention"], 3)
