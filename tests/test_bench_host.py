@@ -21,6 +21,27 @@ def test_block_and_stack_flops():
     assert bench.stack_flops(4096, 16384, 512) / 1e12 == pytest.approx(339.2, abs=0.1)
 
 
+def test_launch_timer_work_counts():
+    """The per-launch work the bench divides the launch timer's times by: the
+    three MFMA kernels add up to the oracle's block FLOP count, and the
+    memory-bound kernels' bytes are those of one pass over their operands."""
+    flop = {k: w for k, (_, w, unit) in bench.TIMED.items() if unit == "flop"}
+    assert set(flop) == {"in_proj", "attention", "out_proj"}
+    for n in (96, 4608, 8704):
+        assert sum(w(n) for w in flop.values()) == O.block_flops(n)
+    _, ln, unit = bench.TIMED["ln_modulate"]
+    assert unit == "byte" and ln(4608) == 4608 * 3072 * (4 + 2)               # fp32 in, bf16 out
+    _, qk, unit = bench.TIMED["qk_norm_rope"]
+    assert unit == "byte" and qk(4608) == 4608 * (2 * 3072 * 2 * 2 + 64 * 2 * 4)  # q, k in/out + table
+    # the kinds the library's timer knows, numbered as the C header numbers them
+    import re
+    import latent_flow_matching_flux3_amd._lib as LL
+    assert set(bench.TIMED) == set(LL.TIMER_KINDS)
+    header = open(os.path.join(ROOT, "include", "flux3_dit.h")).read()
+    defs = {m.group(1).lower(): int(m.group(2)) for m in re.finditer(r"#define FLUX3_TIMER_(\w+) (\d+)", header)}
+    assert defs == LL.TIMER_KINDS
+
+
 def test_code_digest_ignores_comments_and_whitespace(tmp_path):
     a = tmp_path / "a.hip"
     a.write_text("// header\nint f(int x) {\n  return x + 1;  /* one */\n}\n")
