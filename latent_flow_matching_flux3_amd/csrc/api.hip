@@ -793,51 +793,67 @@ struct StackWs {
 // until stage 2: they run on a second HIP stream beside it and fill CUs the
 // image stream's kernels leave idle (at 4096 image rows the output projection
 // has 192 tiles for 256 CUs, and the attention's second round of workgroups
-// is half full).  One side stream and one pair of fork / join events per
-// device, created on first use.  Each event record and the wait on it happen
-// under one lock: another caller recording the fork event in between would
-// let this call's side work start before its inputs are ready.  Not used
-// while the caller's stream is being captured into a graph (work another
-// thread queued on a forked side stream would land in that graph); stage 1
-// then runs on the caller's stream alone.
+// is half full; at 64 + 32 rows both streams' weight streams overlap).  One
+// side stream and one pair of fork / join events per device, created on
+// first use, and not while the caller's stream is being captured (then
+// stage 1 runs on the caller's stream alone).  side_fork takes the device's
+// side-stream lock and side_join releases it: between them no other call can
+// queue work on the side stream, which under capture would land in the
+// caller's graph, and no other call can record the fork event in between
+// (that would let this call's side work start before its inputs are ready).
+// Under capture the fork's event record and wait put the side stream into the
+// capture, and the join brings its work back before the capture ends.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
 };
-std::mutex g_side_mu;
+std::mutex g_side_mu;  // guards creation
 SideStream g_side[64];
 
 // The current device's side stream, made to wait for everything queued on
-// `main` so far; null when there is none to use (capture, HIP failure).
-const SideStream* side_fork(hipStream_t main) {
+// `main` so far, with its lock held; null when there is none to use (HIP
+// failure, or not created yet while `main` is being captured).
+SideStream* side_fork(hipStream_t main) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(main, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  if (hipStreamIsCapturing(main, &cs) != hipSuccess) return nullptr;
+  const bool capturing = cs != hipStreamCaptureStatusNone;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lock(g_side_mu);
   SideStream& sd = g_side[dev];
-  if (sd.s == nullptr) {
-    SideStream x;
-    if (hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&x.join, hipEventDisableTiming) != hipSuccess) {
-      if (x.fork) (void)hipEventDestroy(x.fork);
-      (void)hipStreamDestroy(x.s);
-      return nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    if (sd.s == nullptr) {
+      if (capturing) return nullptr;
+      hipStream_t st = nullptr;
+      hipEvent_t f = nullptr, j = nullptr;
+      if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+      if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+          hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+        if (f) (void)hipEventDestroy(f);
+        (void)hipStreamDestroy(st);
+        return nullptr;
+      }
+      sd.fork = f;
+      sd.join = j;
+      sd.s = st;
     }
-    sd = x;
   }
-  if (hipEventRecord(sd.fork, main) != hipSuccess || hipStreamWaitEvent(sd.s, sd.fork, 0) != hipSuccess)
+  sd.mu.lock();
+  if (hipEventRecord(sd.fork, main) != hipSuccess || hipStreamWaitEvent(sd.s, sd.fork, 0) != hipSuccess) {
+    sd.mu.unlock();
     return nullptr;
+  }
   return &sd;
 }
 
-// `main` waits for everything queued on the side stream so far.
-int side_join(const SideStream* sd, hipStream_t main) {
-  std::lock_guard<std::mutex> lock(g_side_mu);
+// `main` waits for everything queued on the side stream so far; releases the
+// lock side_fork took (also when it fails).
+int side_join(SideStream* sd, hipStream_t main) {
   const hipError_t e = hipEventRecord(sd->join, sd->s);
+  const hipError_t f = e == hipSuccess ? hipStreamWaitEvent(main, sd->join, 0) : e;
+  sd->mu.unlock();
   REQUIRE(e == hipSuccess, FLUX3_EHIP, "stage-1 join record: %s", hipGetErrorString(e));
-  const hipError_t f = hipStreamWaitEvent(main, sd->join, 0);
   REQUIRE(f == hipSuccess, FLUX3_EHIP, "stage-1 join wait: %s", hipGetErrorString(f));
   return FLUX3_OK;
 }
@@ -1024,7 +1040,7 @@ int stack_forward_unchecked(const flux3_model_weights* w, const uint16_t* img, i
 
   // a10: stage 1, each stream on its own rows with its own blocks; the
   // streams after the image one on the side stream when there is one.
-  const SideStream* side = n_modes > 1 ? side_fork(stream) : nullptr;
+  SideStream* side = n_modes > 1 ? side_fork(stream) : nullptr;
   const BlockWs sws = side ? carve_block_ws(s.side_ws, side_rows(n_cond, n_txt)) : bws;
   for (int i = 0; i < n_modes; ++i) {
     const int m = modes[i];
@@ -1377,7 +1393,7 @@ int stack_cfg_unchecked(const flux3_model_weights* w, const uint16_t* img, const
   // copy of the shared streams.  References and texts run on the side stream
   // when there is one.
   const int nt = r.n_t0 + r.n_t1;
-  const SideStream* side = (r.n_cond > 0 || nt > 0) ? side_fork(stream) : nullptr;
+  SideStream* side = (r.n_cond > 0 || nt > 0) ? side_fork(stream) : nullptr;
   const BlockWs sws = side ? carve_block_ws(s.side_ws, side_rows(r.n_cond, nt)) : bws;
   hipStream_t s1 = side ? side->s : stream;
   SegTable one{};
