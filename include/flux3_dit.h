@@ -359,8 +359,10 @@ size_t flux3_stack_workspace_size(int n_img, int n_cond, int n_txt);
  *   v     : device output [n_img][128] fp32
  * Stage 1's streams after the image one (references, text) run on a second
  * HIP stream that the library keeps per device, forked from `stream` and
- * joined back to it before stage 2 (so the call stays ordered on `stream`);
- * while `stream` is being captured into a graph, everything runs on `stream`.
+ * joined back to it before stage 2 (so the call stays ordered on `stream`;
+ * under graph capture the fork and join are part of the captured graph).
+ * That stream is created by the first call on a device that is not under
+ * capture; until then everything runs on `stream`.
  */
 int flux3_stack_forward(const flux3_model_weights* w, const uint16_t* img, int n_img,
                         const uint16_t* cond, int n_cond, const uint16_t* txt, int n_txt,
