@@ -129,13 +129,23 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(bf16* __restrict__ q,
   const float sn[4] = {t0.y, t0.w, t1.y, t1.w};
   const bf16x8 qs = *(const bf16x8*)(q_scale + d0);
   const bf16x8 ks = *(const bf16x8*)(k_scale + d0);
+  // All three head vectors are loaded before any is stored: the rows are
+  // updated in place, so a load after a store would wait for that store.
+  bf16* ptrs[3];
+  bf16x8 cv[3];
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
     const int hv = pass * 16 + vec_id;  // 0..47
     const bool is_k = hv >= kHeads;
     const int head = is_k ? hv - kHeads : hv;
-    bf16* ptr = (is_k ? k + (size_t)tok * ldk : q + (size_t)tok * ldq) + head * kHeadDim + d0;
-    bf16x8 c = *(const bf16x8*)ptr;
+    ptrs[pass] = (is_k ? k + (size_t)tok * ldk : q + (size_t)tok * ldq) + head * kHeadDim + d0;
+    cv[pass] = *(const bf16x8*)ptrs[pass];
+  }
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const bool is_k = pass * 16 + vec_id >= kHeads;
+    bf16* ptr = ptrs[pass];
+    const bf16x8 c = cv[pass];
     float v[8];
     float ss = 0.f;
 #pragma unroll
