@@ -471,9 +471,10 @@ int flux3_sigmas(int steps, double alpha, float* out);
  * written, min(launches recorded, capacity).  Destroys the events and
  * disarms even when it fails.  FLUX3_EINVAL if the timer is not armed;
  * FLUX3_EHIP if an event could not be read (its entry is 0). */
-#define FLUX3_TIMER_IN_PROJ 0       /* a4 + a5: the fused input projection (at most 128 rows:
-                                       with a6 in its epilogue) */
-#define FLUX3_TIMER_QK_NORM_ROPE 1  /* a6 where it runs as a kernel of its own (over 128 rows) */
+#define FLUX3_TIMER_IN_PROJ 0       /* a4 + a5: the fused input projection (bf16 blocks of at
+                                       most 128 or over 256 rows: with a6 in its epilogue) */
+#define FLUX3_TIMER_QK_NORM_ROPE 1  /* a6 where it runs as a kernel of its own (bf16 blocks of
+                                       129..256 rows, fp8r blocks) */
 #define FLUX3_TIMER_ATTENTION 2     /* a7, every row group of the call */
 #define FLUX3_TIMER_OUT_PROJ 3      /* a8, with its split-K reduce when one runs (at most 128
                                        rows, inside a stage: with the next block's a3) */

@@ -194,9 +194,11 @@ class TimedLaunch {
 };
 
 // a4 + a5: [q | k | v] and h_mlp = silu(a) * b in one product over w_in;
-// with q_scale (skinny products only), also a6 on q and k in the epilogue.
+// with q_scale (where gemm_fuses_qk_norm holds), also a6 on q and k in the
+// epilogue, and zero[0 .. nzero) cleared on the 256x256 kernel.
 void in_proj(const bf16* xm, int n, const bf16* w_in, bf16* qkv, bf16* h, int ldh, hipStream_t st,
-             const bf16* q_scale = nullptr, const bf16* k_scale = nullptr, const float* table = nullptr) {
+             const bf16* q_scale = nullptr, const bf16* k_scale = nullptr, const float* table = nullptr,
+             int* zero = nullptr, int nzero = 0) {
   GemmArgs g{};
   g.A = xm;
   g.lda = kHidden;
@@ -213,6 +215,8 @@ void in_proj(const bf16* xm, int n, const bf16* w_in, bf16* qkv, bf16* h, int ld
   g.qk_scale_q = q_scale;
   g.qk_scale_k = k_scale;
   g.rope_table = q_scale ? table : nullptr;
+  g.zero = nzero > 0 ? zero : nullptr;
+  g.nzero = nzero;
   launch_gemm(g, st);
 }
 
@@ -259,7 +263,11 @@ bool block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
                              hipStream_t st, const SegTable* attn = nullptr, bool ln_ready = false,
                              bool next_ln = false) {
   const bool fp8 = w->w_in_fp8 != nullptr;
-  const bool fuse_qk = !fp8 && ws.nzero == 0 && gemm_skinny_used(n, kWInRows, kHidden);
+  // a6 in the in-projection's epilogue: on the 256x256 kernel, which also
+  // clears the workspace's counters, or on the skinny kernel where there are
+  // none to clear.
+  const bool ring_qk = !fp8 && gemm_ring_used(n, kWInRows, kHidden);
+  const bool fuse_qk = ring_qk || (!fp8 && ws.nzero == 0 && gemm_skinny_used(n, kWInRows, kHidden));
   uint8_t* const xm8 = (uint8_t*)ws.xm;
   if (fp8) {
     // a3 with the rowwise FP8 quantization fused; a4 + a5 as an fp8r product
@@ -291,12 +299,12 @@ bool block_forward_unchecked(float* x, int n, const SegTable& seg, const float* 
       launch_ln_modulate(x, kHidden, ws.xm, kHidden, n, seg, mod, 3 * kHidden, st);
     }
     // a4 + a5: q | k | v into qkv; SwiGLU output into the last 9216 columns of
-    // cat.  Products of at most 128 rows run on the skinny kernel, which also
-    // applies a6 (when no counters are waiting for the norm kernel to clear them).
+    // cat.  Except on the mid-size kernel (129 .. 256 rows), the epilogue also
+    // applies a6.
     TimedLaunch t(FLUX3_TIMER_IN_PROJ, n, st);
     if (fuse_qk)
       in_proj(ws.xm, n, B(w->w_in), ws.qkv, ws.cat + kHidden, kWOutCols, st, B(w->q_scale), B(w->k_scale),
-              table);
+              table, ring_qk ? ws.zero : nullptr, ring_qk ? ws.nzero : 0);
     else
       in_proj(ws.xm, n, B(w->w_in), ws.qkv, ws.cat + kHidden, kWOutCols, st);
   }

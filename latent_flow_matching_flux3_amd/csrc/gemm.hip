@@ -306,6 +306,14 @@ void launch_gemm_fp8(const GemmArgs& g, hipStream_t st) {
 
 bool gemm_skinny_used(int m, int n, int k) { return skinny_shape(m, n, k); }
 
+// The kernel launch_gemm picks for a product without split-K or stream-K
+// scratch (the in-projection): 256x256 tiles once there are 192 of them.
+bool gemm_ring_used(int m, int n, int k) {
+  return m > 0 && !skinny_shape(m, n, k) && n % 256 == 0 && (long)((m + 255) / 256) * (n / 256) >= 192;
+}
+
+bool gemm_fuses_qk_norm(int m, int n, int k) { return skinny_shape(m, n, k) || gemm_ring_used(m, n, k); }
+
 bool gemm_fuses_next_ln(int m, int n, int k, size_t scratch_bytes) {
   if (!skinny_shape(m, n, k) || n != kHidden) return false;
   const int d = skinny_split(n, k);
@@ -395,7 +403,6 @@ void launch_gemm(const GemmArgs& g, hipStream_t st) {
     run_skinny(g, st);
     return;
   }
-  const long big_tiles = (long)((g.M + 255) / 256) * (g.N / 256);
   // Gated residual and fp32 products with too few tiles to fill the chip and
   // a long K (the text stream's and small batches' output projection, the text
   // embedding): split K over the idle CUs when the caller lent scratch for the
@@ -427,7 +434,7 @@ void launch_gemm(const GemmArgs& g, hipStream_t st) {
       return;
     }
   }
-  if (g.N % 256 == 0 && big_tiles >= 192) {
+  if (gemm_ring_used(g.M, g.N, g.K)) {
     run_ring<256, 256, 2, 2, 32, 5, 1>(g, st);
   } else if (g.N % 128 == 0) {
     run_regs<128, 128, 2, 2>(g, st);

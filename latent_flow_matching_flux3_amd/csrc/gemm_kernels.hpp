@@ -146,6 +146,67 @@ struct TileWalk {
 // sk_store_part.  They are added in part order whoever holds which part:
 // (P0 + P1) + P2, with own_last when acc is P2, else acc is P0 or P1 and
 // (acc + other) + P2 is the same sum exactly (IEEE addition commutes).
+// The q or k columns of a wave tile 128 columns wide (one head: wcol0 is a
+// multiple of 128) with the head's RMSNorm and RoPE applied before the store,
+// in the arithmetic of qk_norm_rope_kernel: the projection rounded to bf16,
+// then x / sqrt(mean_128(x^2) + 1e-6) * scale, then each pair (2p, 2p+1)
+// rotated by the row's table entry p, rounded to bf16.  Lane l holds 64 of
+// the 128 values of rows wrow0 + 32 i + l % 32 (four consecutive columns per
+// register group); lane l ^ 32 holds the other 64.
+template <class T>
+__device__ __forceinline__ void qk_norm_rope_tile(const GemmArgs& g, floatx16 (&acc)[T::FM][T::FN], int wrow0,
+                                                  int wcol0, int lane) {
+  static_assert(T::FN * 32 == kHeadDim, "one head per wave tile");
+  const int lr = lane & 31;
+  const bf16* scale = wcol0 >= kHidden ? g.qk_scale_k : g.qk_scale_q;
+  bf16x4 sc[T::FN][4];
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) sc[j][g4] = *(const bf16x4*)(scale + 32 * j + frag_col(g4, lane));
+  bf16* C = (bf16*)g.C;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    const int row = wrow0 + 32 * i + lr;
+    // (cos, sin) of this lane's pairs; rows past M-1 read row M-1's
+    const float* t = g.rope_table + (size_t)min(row, g.M - 1) * kHeadDim;
+    float4 tb[T::FN][4];
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) tb[j][g4] = *(const float4*)(t + 32 * j + frag_col(g4, lane));
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float v = to_f32(to_bf16(acc[i][j][r]));
+        s += v * v;
+      }
+    s += __shfl_xor(s, 32, 64);
+    const float rn = 1.0f / sqrtf(s * (1.0f / kHeadDim) + 1e-6f);
+    if (row < g.M) {
+      bf16* crow = C + (size_t)row * g.ldc + wcol0;
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 tt = tb[j][g4];  // (cos, sin) of pairs c/2 and c/2 + 1
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = to_f32(to_bf16(acc[i][j][4 * g4 + e])) * rn * to_f32(sc[j][g4][e]);
+          bf16x4 o;
+          o[0] = to_bf16(v[0] * tt.x - v[1] * tt.y);
+          o[1] = to_bf16(v[0] * tt.y + v[1] * tt.x);
+          o[2] = to_bf16(v[2] * tt.z - v[3] * tt.w);
+          o[3] = to_bf16(v[2] * tt.w + v[3] * tt.z);
+          *(bf16x4*)(crow + 32 * j + frag_col(g4, lane)) = o;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <class T, GemmEpi EPI, bool SC = false, bool MG = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::FM][T::FN],
                                          int wrow0, int wcol0, const float* sc = nullptr,
@@ -172,6 +233,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::F
     if constexpr (SC) return sc[32 * i + lr];
     else return 1.f;
   };
+  if constexpr (EPI == GemmEpi::kInProj && !SC && T::FN * 32 == kHeadDim) {
+    if (g.rope_table != nullptr && wcol0 < 2 * kHidden) {  // wave-uniform
+      qk_norm_rope_tile<T>(g, acc, wrow0, wcol0, lane);
+      return;
+    }
+  }
   if constexpr (EPI == GemmEpi::kStoreBf16 || EPI == GemmEpi::kInProj) {
     if (EPI == GemmEpi::kStoreBf16 || wcol0 < 3 * kHidden) {
       bf16* C = (bf16*)g.C;
@@ -504,6 +571,11 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   const long sk_s0 = (long)sk_v * sk_S / gridDim.x, sk_s1 = (long)(sk_v + 1) * sk_S / gridDim.x;
   const int sk_t0 = (int)(sk_s0 / KTT);
   const int count = SK ? (sk_s1 > sk_s0 ? (int)((sk_s1 - 1) / KTT) - sk_t0 + 1 : 0) : walk.count;
+  if constexpr (EPI == GemmEpi::kInProj) {
+    // counters the kernels after this one expect at zero
+    if (blockIdx.x == 0 && g.zero != nullptr)
+      for (int i = threadIdx.x; i < g.nzero; i += NW * 64) g.zero[i] = 0;
+  }
   if (count == 0) return;
 
   const int tid = threadIdx.x;

@@ -73,13 +73,18 @@ struct GemmArgs {
   int* sk_cnt;
   float* sk_part;
   size_t sk_bytes;
-  // kInProj on the skinny kernel (M <= 128): optional QK RMSNorm + RoPE in
+  // kInProj where gemm_fuses_qk_norm holds: optional QK RMSNorm + RoPE in
   // the epilogue (q_scale / k_scale bf16 [128], rope_table [M][64][2] as for
   // launch_qk_norm_rope): the q and k columns are stored normalised and
   // rotated, so no separate norm kernel runs.  Null: plain q | k | v stores.
+  // zero[0 .. nzero), if given, is cleared by the 256x256 kernel's first
+  // workgroup (the counters launch_qk_norm_rope would otherwise clear; the
+  // skinny kernel clears none).
   const bf16* qk_scale_q;
   const bf16* qk_scale_k;
   const float* rope_table;
+  int* zero;
+  int nzero;
   // kGatedResidual on the skinny kernel split over K: optional output of the
   // next block's LayerNorm + modulation of the updated rows (same mod and
   // segments: shift at mod + s * mod_stride, scale 3072 further), bf16 with
@@ -96,9 +101,14 @@ size_t gemm_split_ws_bytes(int m, int n, int k);
 // a split), else counters (gemm_sk_counters of them, first) and partial
 // slots.  The counters must be zero before the first launch.
 size_t gemm_sk_ws_bytes(int m, int n, int k);
-// True where launch_gemm runs the skinny kernel (M <= 128 rows), whose
-// in-projection epilogue can apply the QK norm (GemmArgs::rope_table).
+// True where launch_gemm runs the skinny kernel (M <= 128 rows).
 bool gemm_skinny_used(int m, int n, int k);
+// True where a kInProj product of this shape runs on a kernel whose
+// epilogue applies the QK norm (GemmArgs::rope_table): the skinny kernel, or
+// the 256x256 kernel (each wave's 128 columns of q or k are one head).
+bool gemm_fuses_qk_norm(int m, int n, int k);
+// True where that kernel is the 256x256 one (it clears GemmArgs::zero).
+bool gemm_ring_used(int m, int n, int k);
 // True where a kGatedResidual product of this shape, lent `scratch_bytes` of
 // split scratch, runs split over K on the skinny kernel and so applies
 // GemmArgs::ln_out in its reduce.
