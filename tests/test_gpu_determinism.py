@@ -123,3 +123,31 @@ def test_stack_twice(L):
     a, b = _twice(run)
     assert np.isfinite(a.cpu().numpy()).all()
     _equal(a, b, "stack_forward")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_block_dirty_workspace(L, fp8):
+    """A block workspace needs no initial contents: its counters (the balanced
+    attention's and the stream-K output projection's) are cleared inside the
+    block, by the in-projection above 256 rows or by the QK norm kernel where
+    that runs on its own (fp8r blocks).  The same block on a workspace of
+    0xFF bytes (every counter -1) and on a zeroed one: equal bit for bit."""
+    lay = syn.Layout(48, 48, 513)          # 2817 rows: balanced attention and stream-K
+    n = lay.n_total
+    ids = O.build_ids(lay.img_h, lay.img_w, lay.n_txt)
+    segs = [0, lay.n_img, n]
+    blk = L.PackedBlock(upload(syn.block_weights(65, "single_blocks.0")), fp8=fp8)
+    x0 = dev(syn.block_activations(66, n)).float()
+    mods = dev(syn.normal_f32((2, 3, 3072), 0.5, 67, "mods"))
+    table = L.flux3_rope_table(dev(torch.tensor(ids, dtype=torch.float32)))
+    ws = L.workspace(L.flux3_block_workspace_size(n))
+    say(f"dirty workspace block n={n} fp8={fp8}")
+    out = []
+    for fill in (0, 255):
+        ws.fill_(fill)
+        x = x0.clone()
+        L.flux3_block_forward(x, segs, mods, blk, table, ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(x).all().item()
+        out.append(x)
+    _equal(out[0], out[1], f"block on a dirty workspace fp8={fp8}")
