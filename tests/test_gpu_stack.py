@@ -448,6 +448,30 @@ def test_stack_fp8r(L):
     assert_agree(f64(v), ref, "stack fp8r", cos_min=0.999, rel_max=FP8_REL_MAX)
 
 
+@pytest.mark.parametrize("n,qk_kernel", [(200, True), (300, False)])
+def test_launch_timer_block_kinds(L, n, qk_kernel):
+    """Which kernels a bf16 block launches, as the launch timer sees them: at
+    129..256 rows the QK norm + RoPE is a kernel of its own; above 256 rows
+    the in-projection applies it in its epilogue, so the block records
+    LayerNorm, in-projection, attention and output projection only."""
+    from gpu_util import upload
+    lay = syn.Layout(10, 10, n - 100)
+    ids = O.build_ids(lay.img_h, lay.img_w, lay.n_txt)
+    segs = [0, lay.n_img, n]
+    blk = L.PackedBlock(upload(syn.block_weights(72, "single_blocks.0")))
+    x = dev(syn.block_activations(73, n)).float()
+    mods = dev(syn.normal_f32((2, 3, 3072), 0.5, 74, "mods"))
+    table = L.flux3_rope_table(dev(torch.tensor(ids, dtype=torch.float32)))
+    ws = L.workspace(L.flux3_block_workspace_size(n))
+    say(f"launch timer: block n={n}")
+    L.flux3_timer_start(list(L.TIMER_KINDS), 16)
+    L.flux3_block_forward(x, segs, mods, blk, table, ws)
+    recs = L.flux3_timer_stop(16)
+    expect = ["ln_modulate", "in_proj"] + (["qk_norm_rope"] if qk_kernel else []) + ["attention", "out_proj"]
+    assert [k for k, _, _ in recs] == expect
+    assert all(r == n and ms > 0 for _, r, ms in recs)
+
+
 def test_launch_timer(L):
     """The launch timer records the block's five kernels in every block call of
     a stack step, with the call's rows, on the stream each runs on (the text
