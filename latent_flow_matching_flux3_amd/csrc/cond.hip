@@ -46,18 +46,24 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvBatch batch, int rows, in
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nchunk = K / 8;
+  // f(x) in registers: every load issued first (chunks past K read the last
+  // chunk again and are then zeroed), so the wave waits for x once, not once
+  // per element.
   float xv[kGemvMaxChunksPerLane][8];
 #pragma unroll
   for (int i = 0; i < kGemvMaxChunksPerLane; ++i) {
-    const int c = lane + 64 * i;
+    const float* xp = x + min(lane + 64 * i, nchunk - 1) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xv[i][e] = xp[e];
+  }
+#pragma unroll
+  for (int i = 0; i < kGemvMaxChunksPerLane; ++i) {
+    const bool valid = lane + 64 * i < nchunk;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float val = 0.f;
-      if (c < nchunk) {
-        val = x[c * 8 + e];
-        if (silu_x) val = val / (1.0f + __expf(-val));
-      }
-      xv[i][e] = val;
+      float val = xv[i][e];
+      if (silu_x) val = val / (1.0f + __expf(-val));
+      xv[i][e] = valid ? val : 0.f;
     }
   }
   const int r0 = (blockIdx.x * 4 + wave) * RPW;
