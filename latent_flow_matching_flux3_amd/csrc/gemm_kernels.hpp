@@ -54,6 +54,29 @@ __device__ __forceinline__ floatx16 mma(const bf16x8& x_frag, const bf16x8& w_fr
 }
 __device__ __forceinline__ int frag_col(int g4, int lane) { return 8 * g4 + 4 * (lane >> 5); }
 
+// Store half of one fragment row's 32 bf16 values as 16-byte accesses: lo and
+// hi are groups 2q and 2q + 1 (columns frag_col(2q, lane) .. +3 and
+// frag_col(2q + 1, lane) .. +3 of lane l's row, and lane l ^ 32's).  The two
+// lanes first trade groups (v_permlane32_swap moves the upper half's first
+// operand and the lower half's second), so lane l holds columns 16q .. 16q+7
+// and lane l + 32 columns 16q+8 .. 16q+15; each store then writes 32
+// contiguous bytes of the row per lane pair instead of two 8-byte pieces.
+// p: the fragment's first column in the row.  Lanes l and l + 32 hold the
+// same row, so both are active or neither.
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_frag_half(bf16* p, int q, bf16x4 lo, bf16x4 hi, int lane) {
+  u32x2_t a = __builtin_bit_cast(u32x2_t, lo), b = __builtin_bit_cast(u32x2_t, hi);
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a[d], b[d], false, false);
+    a[d] = r[0];
+    b[d] = r[1];
+  }
+  const u32x4_t w = {a[0], a[1], b[0], b[1]};
+  *(u32x4_t*)(p + 16 * q + 8 * (lane >> 5)) = w;
+}
+
 template <int BM_, int BN_, int WM_, int WN_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
@@ -190,17 +213,21 @@ __device__ __forceinline__ void qk_norm_rope_tile(const GemmArgs& g, floatx16 (&
 #pragma unroll
       for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 tt = tb[j][g4];  // (cos, sin) of pairs c/2 and c/2 + 1
-          float v[4];
+        for (int q = 0; q < 2; ++q) {
+          bf16x4 o[2];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = to_f32(to_bf16(acc[i][j][4 * g4 + e])) * rn * to_f32(sc[j][g4][e]);
-          bf16x4 o;
-          o[0] = to_bf16(v[0] * tt.x - v[1] * tt.y);
-          o[1] = to_bf16(v[0] * tt.y + v[1] * tt.x);
-          o[2] = to_bf16(v[2] * tt.z - v[3] * tt.w);
-          o[3] = to_bf16(v[2] * tt.w + v[3] * tt.z);
-          *(bf16x4*)(crow + 32 * j + frag_col(g4, lane)) = o;
+          for (int u = 0; u < 2; ++u) {
+            const int g4 = 2 * q + u;
+            const float4 tt = tb[j][g4];  // (cos, sin) of pairs c/2 and c/2 + 1
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = to_f32(to_bf16(acc[i][j][4 * g4 + e])) * rn * to_f32(sc[j][g4][e]);
+            o[u][0] = to_bf16(v[0] * tt.x - v[1] * tt.y);
+            o[u][1] = to_bf16(v[0] * tt.y + v[1] * tt.x);
+            o[u][2] = to_bf16(v[2] * tt.z - v[3] * tt.w);
+            o[u][3] = to_bf16(v[2] * tt.w + v[3] * tt.z);
+          }
+          store_frag_half(crow + 32 * j, q, o[0], o[1], lane);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -251,14 +278,17 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::F
 #pragma unroll
           for (int j = 0; j < T::FN; ++j) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-              const float4 f = f4(i, j, g4, sa);
-              bf16x4 v;
-              v[0] = to_bf16(f.x);
-              v[1] = to_bf16(f.y);
-              v[2] = to_bf16(f.z);
-              v[3] = to_bf16(f.w);
-              *(bf16x4*)(crow + 32 * j + frag_col(g4, lane)) = v;
+            for (int q = 0; q < 2; ++q) {
+              bf16x4 v[2];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const float4 f = f4(i, j, 2 * q + u, sa);
+                v[u][0] = to_bf16(f.x);
+                v[u][1] = to_bf16(f.y);
+                v[u][2] = to_bf16(f.z);
+                v[u][3] = to_bf16(f.w);
+              }
+              store_frag_half(crow + 32 * j, q, v[0], v[1], lane);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -277,14 +307,17 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[T::F
 #pragma unroll
           for (int p = 0; p < T::FN / 2; ++p) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-              const float4 a = f4(i, 2 * p, g4, sa), b = f4(i, 2 * p + 1, g4, sa);
-              bf16x4 v;
-              v[0] = to_bf16(silu_f(a.x) * b.x);
-              v[1] = to_bf16(silu_f(a.y) * b.y);
-              v[2] = to_bf16(silu_f(a.z) * b.z);
-              v[3] = to_bf16(silu_f(a.w) * b.w);
-              *(bf16x4*)(hrow + 32 * p + frag_col(g4, lane)) = v;
+            for (int q = 0; q < 2; ++q) {
+              bf16x4 v[2];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const float4 a = f4(i, 2 * p, 2 * q + u, sa), b = f4(i, 2 * p + 1, 2 * q + u, sa);
+                v[u][0] = to_bf16(silu_f(a.x) * b.x);
+                v[u][1] = to_bf16(silu_f(a.y) * b.y);
+                v[u][2] = to_bf16(silu_f(a.z) * b.z);
+                v[u][3] = to_bf16(silu_f(a.w) * b.w);
+              }
+              store_frag_half(hrow + 32 * p, q, v[0], v[1], lane);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
