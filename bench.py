@@ -37,11 +37,11 @@ COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
 # its 4608-row launches inside stack steps (as its roofline is timed); the
 # others are of their kernel alone (--only).
 TRAFFIC = {
-    "gemm_in_proj_swiglu": (1494.5e6 + 170.2e6, {"gemm_kernels.hpp": "8eb2e4fd48943eed", "gemm.hip": "451c34be83752b6c",
-                                                 "kernels.hpp": "f29491e4dbacf02f", "common.hpp": "a628a66ce9fdd5dc"}),
-    "gemm_out_proj_gated": (747.8e6 + 59.3e6, {"gemm_kernels.hpp": "8eb2e4fd48943eed", "gemm.hip": "451c34be83752b6c",
-                                               "kernels.hpp": "f29491e4dbacf02f", "common.hpp": "a628a66ce9fdd5dc"}),
-    "attention": (356.6e6 + 90.1e6, {"attention.hip": "bbd9a581ae964ab5", "kernels.hpp": "f29491e4dbacf02f", "common.hpp": "a628a66ce9fdd5dc"}),
+    "gemm_in_proj_swiglu": (1491.8e6 + 170.2e6, {"gemm_kernels.hpp": "c6587cfc6a48c98d", "gemm.hip": "f10221f408a8d22b",
+                                                 "kernels.hpp": "30f6016329aff61f", "common.hpp": "a628a66ce9fdd5dc"}),
+    "gemm_out_proj_gated": (751.6e6 + 59.3e6, {"gemm_kernels.hpp": "c6587cfc6a48c98d", "gemm.hip": "f10221f408a8d22b",
+                                               "kernels.hpp": "30f6016329aff61f", "common.hpp": "a628a66ce9fdd5dc"}),
+    "attention": (357.5e6 + 90.0e6, {"attention.hip": "bbd9a581ae964ab5", "kernels.hpp": "30f6016329aff61f", "common.hpp": "a628a66ce9fdd5dc"}),
 }
 
 

@@ -91,6 +91,7 @@ size_t split_bytes(int m, int n, int s) { return (size_t)s * ((m + 255) / 256) *
 // longest workgroup's work shrinks by at least 5%: the output projection at
 // 4608 rows (216 tiles of 384 slices on 256 CUs: 324 slices per workgroup
 // against 384) or 4096 rows (192 tiles: 288 against 384).
+constexpr int kSkGroupM = 6;                    // tile rows per group of the tile order
 constexpr int kSkWaves = 4;                     // waves per workgroup (2 x 2)
 constexpr size_t kSkPartBytes = 128 * 128 * 4;  // one wave tile, fp32
 
@@ -429,8 +430,10 @@ void launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (gated && g.sk_cnt != nullptr) {
     const size_t need = gemm_sk_ws_bytes(g.M, g.N, g.K);
     if (need > 0 && need <= g.sk_bytes) {
+      GemmArgs h = g;
+      h.group_m = kSkGroupM;
       hipLaunchKernelGGL((gemm::gemm_ring_kernel<256, 256, 2, 2, 32, 5, 1, GemmEpi::kGatedResidual, true>),
-                         dim3(cu_count()), dim3(256), 0, st, g, (g.M + 255) / 256, g.N / 256);
+                         dim3(cu_count()), dim3(256), 0, st, h, (g.M + 255) / 256, g.N / 256);
       return;
     }
   }

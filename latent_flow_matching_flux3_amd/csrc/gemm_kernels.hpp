@@ -95,8 +95,9 @@ struct Tile {
 // by column, so neighbouring positions share A rows or B rows (3 rows of A,
 // 4.5 MB at K = 3072, about one XCD's L2; 3 measured faster than 2, 4, 6 or 8
 // for the 4608-row in-projection and at the step level).
-__device__ __forceinline__ void grouped_coords(int lin, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int GM = 3;
+// GM: tile rows per group (the stream-K output projection passes its own).
+__device__ __forceinline__ void grouped_coords(int lin, int tiles_m, int tiles_n, int& tm, int& tn,
+                                               int GM = 3) {
   const int group = lin / (GM * tiles_n);
   const int first_m = group * GM;
   const int gsize = min(tiles_m - first_m, GM);
@@ -604,6 +605,7 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   const long sk_s0 = (long)sk_v * sk_S / gridDim.x, sk_s1 = (long)(sk_v + 1) * sk_S / gridDim.x;
   const int sk_t0 = (int)(sk_s0 / KTT);
   const int count = SK ? (sk_s1 > sk_s0 ? (int)((sk_s1 - 1) / KTT) - sk_t0 + 1 : 0) : walk.count;
+  const int sk_gm = g.group_m > 0 ? g.group_m : 3;  // tile rows per group of the stream-K order
   if constexpr (EPI == GemmEpi::kInProj) {
     // counters the kernels after this one expect at zero
     if (blockIdx.x == 0 && g.zero != nullptr)
@@ -652,7 +654,7 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     if constexpr (SK) {
       int lin, kb;
       item(i, lin, kb, ld_len);
-      grouped_coords(lin, tiles_m, tiles_n, tm, tn);
+      grouped_coords(lin, tiles_m, tiles_n, tm, tn, sk_gm);
       k0 = (size_t)kb * BK;
     } else {
       int split;
@@ -788,7 +790,7 @@ void gemm_ring_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     int tm, tn, split = 0;
     if constexpr (SK) {
       item(i, cur_lin, cur_kb, cur_len);
-      grouped_coords(cur_lin, tiles_m, tiles_n, tm, tn);
+      grouped_coords(cur_lin, tiles_m, tiles_n, tm, tn, sk_gm);
       cur_len = __builtin_amdgcn_readfirstlane(cur_len);
     } else {
       walk.coords(i, tiles_m, tiles_n, splits, tm, tn, split);

@@ -73,6 +73,8 @@ struct GemmArgs {
   int* sk_cnt;
   float* sk_part;
   size_t sk_bytes;
+  // stream-K: tile rows per group of its tile order (0: 3)
+  int group_m;
   // kInProj where gemm_fuses_qk_norm holds: optional QK RMSNorm + RoPE in
   // the epilogue (q_scale / k_scale bf16 [128], rope_table [M][64][2] as for
   // launch_qk_norm_rope): the q and k columns are stored normalised and
