@@ -973,11 +973,133 @@ int check_stack_args(const flux3_model_weights* w, const uint16_t* img, int n_im
   return FLUX3_OK;
 }
 
+// The modulation vectors of one stack pass: per present mode i (in token
+// order) early and single (shift, scale, gate) at mod_early / mod_single +
+// i * 9216, and the final layer's (shift, scale) at mod_final.
+struct CondSlot {
+  float* vec;  // [n_modes][3072]
+  float* mod_early;
+  float* mod_single;
+  float* mod_final;
+};
+
+// Present modes in token order (image, image_cond, text) and their rows.
+int present_modes(int n_img, int n_cond, int n_txt, int* modes, int* counts) {
+  const int all_counts[3] = {n_img, n_cond, n_txt};
+  int n = 0;
+  for (int m = 0; m < 3; ++m)
+    if (all_counts[m] > 0) {
+      modes[n] = m;
+      if (counts) counts[n] = all_counts[m];
+      ++n;
+    }
+  return n;
+}
+
+// GEMV items y_i (+)= W_i f(x_i), launched in batches of kMaxSeg (items of
+// one batch must not depend on each other).
+struct GemvItems {
+  GemvBatch b{};
+  int n = 0;
+  int rows, K;
+  bool silu, acc;
+  hipStream_t st;
+  GemvItems(int rows_, int K_, bool silu_, bool acc_, hipStream_t st_)
+      : rows(rows_), K(K_), silu(silu_), acc(acc_), st(st_) {}
+  void add(const bf16* w, const float* x, float* y) {
+    b.w[n] = w;
+    b.x[n] = x;
+    b.y[n] = y;
+    if (++n == kMaxSeg) flush();
+  }
+  void flush() {
+    if (n > 0) launch_gemv(b, n, rows, K, silu, acc, st);
+    n = 0;
+  }
+};
+
+// Conditioning of sampling steps k0 .. k0 + nk - 1 (nk <= kCondChunk) into
+// slots[0 .. nk): the same GEMVs as a stack pass makes for each step (each
+// row's sum in the same order, so the same bits), batched over the steps so
+// that a launch reads each weight for several steps at once.  The time
+// embeddings of sigma_k0 .. sigma_{k0+nk} and of 0 go to emb.
+constexpr int kCondChunk = 8;
+size_t cond_slot_bytes() {
+  return align256(3 * kHidden * 4) + 2 * align256(3 * 3 * kHidden * 4) + align256(2 * kHidden * 4);
+}
+size_t cond_chunk_bytes() {
+  return kCondChunk * cond_slot_bytes() + align256((kCondChunk + 2) * 256 * 4) +
+         align256((size_t)kCondChunk * 3 * kHidden * 4) + align256((size_t)kCondChunk * kHidden * 4);
+}
+int precompute_cond(const flux3_model_weights* w, const int* modes, int n_modes, const float* sigmas, int k0,
+                    int nk, char* buf, CondSlot* slots, hipStream_t st) {
+  for (int j = 0; j < nk; ++j) {
+    char* p = buf + j * cond_slot_bytes();
+    slots[j].vec = (float*)p;
+    p += align256(3 * kHidden * 4);
+    slots[j].mod_early = (float*)p;
+    p += align256(3 * 3 * kHidden * 4);
+    slots[j].mod_single = (float*)p;
+    p += align256(3 * 3 * kHidden * 4);
+    slots[j].mod_final = (float*)p;
+  }
+  char* p = buf + kCondChunk * cond_slot_bytes();
+  float* emb = (float*)p;  // [nk + 2][256]: emb(sigma_{k0+j}), j <= nk, then emb(0)
+  p += align256((kCondChunk + 2) * 256 * 4);
+  float* hid = (float*)p;  // [nk][n_modes][3072]
+  p += align256((size_t)kCondChunk * 3 * kHidden * 4);
+  float* rh = (float*)p;   // [nk][3072]
+  for (int j0 = 0; j0 < nk + 2; j0 += 4) {  // four embeddings per launch
+    Timesteps ts{};
+    const int nt = std::min(4, nk + 2 - j0);
+    for (int t = 0; t < nt; ++t) ts.t[t] = j0 + t <= nk ? sigmas[k0 + j0 + t] : 0.f;
+    launch_timestep_embedding(ts, nt, emb + (size_t)j0 * 256, st);
+  }
+  const float* emb0 = emb + (size_t)(nk + 1) * 256;
+  // time_in: vec[j][m] = W2 silu(W1 emb(t)), t = sigma_{k0+j} for the image mode, else 0
+  GemvItems l1(kHidden, 256, false, false, st);
+  for (int j = 0; j < nk; ++j)
+    for (int i = 0; i < n_modes; ++i)
+      l1.add(B(w->time_in_w1), modes[i] == 0 ? emb + (size_t)j * 256 : emb0,
+             hid + ((size_t)j * 3 + i) * kHidden);
+  l1.flush();
+  GemvItems l2(kHidden, kHidden, true, false, st);
+  for (int j = 0; j < nk; ++j)
+    for (int i = 0; i < n_modes; ++i)
+      l2.add(B(w->time_in_w2), hid + ((size_t)j * 3 + i) * kHidden, slots[j].vec + (size_t)i * kHidden);
+  l2.flush();
+  if (w->ref_time_in_w1 && w->ref_time_in_w2) {
+    // + ref_time_in(emb(sigma_{k0+j+1})) on every mode
+    GemvItems r1(kHidden, 256, false, false, st);
+    for (int j = 0; j < nk; ++j) r1.add(B(w->ref_time_in_w1), emb + (size_t)(j + 1) * 256, rh + (size_t)j * kHidden);
+    r1.flush();
+    GemvItems r2(kHidden, kHidden, true, true, st);
+    for (int j = 0; j < nk; ++j)
+      for (int i = 0; i < n_modes; ++i)
+        r2.add(B(w->ref_time_in_w2), rh + (size_t)j * kHidden, slots[j].vec + (size_t)i * kHidden);
+    r2.flush();
+  }
+  // modulations: early and single per mode, final adaLN on the image vector
+  GemvItems mods(3 * kHidden, kHidden, true, false, st);
+  for (int j = 0; j < nk; ++j)
+    for (int i = 0; i < n_modes; ++i) {
+      const float* v = slots[j].vec + (size_t)i * kHidden;
+      mods.add(B(w->early_mod[modes[i]]), v, slots[j].mod_early + (size_t)i * 3 * kHidden);
+      mods.add(B(w->single_mod[modes[i]]), v, slots[j].mod_single + (size_t)i * 3 * kHidden);
+    }
+  mods.flush();
+  GemvItems fin(2 * kHidden, kHidden, true, false, st);
+  for (int j = 0; j < nk; ++j) fin.add(B(w->final_ada), slots[j].vec, slots[j].mod_final);
+  fin.flush();
+  return check_launch("sample conditioning");
+}
+
 // One pass of the transformer on checked arguments; workspace = StackWs.
+// pre: this step's conditioning, already computed (precompute_cond), or null.
 int stack_forward_unchecked(const flux3_model_weights* w, const uint16_t* img, int n_img,
                             const uint16_t* cond, int n_cond, const uint16_t* txt, int n_txt,
                             const float* table, float sigma, float sigma_next, float* v,
-                            void* workspace, hipStream_t stream) {
+                            void* workspace, hipStream_t stream, const CondSlot* pre = nullptr) {
   const int n_total = n_img + n_cond + n_txt;
   // Streams present, in token order.
   int modes[3], counts[3], n_modes = 0;
@@ -993,12 +1115,19 @@ int stack_forward_unchecked(const flux3_model_weights* w, const uint16_t* img, i
   const BlockWs bws = carve_block_ws(s.block_ws, n_total);
 
   // a13 / conditioning: per-mode vectors, then the 2 x n_modes modulations and
-  // the final adaLN (SiLU then Linear).
+  // the final adaLN (SiLU then Linear), unless the caller computed them.
+  int rc = FLUX3_OK;
+  if (pre != nullptr) {
+    s.vec = pre->vec;
+    s.mod_early = pre->mod_early;
+    s.mod_single = pre->mod_single;
+    s.mod_final = pre->mod_final;
+  } else {
   int is_image[3];
   for (int i = 0; i < n_modes; ++i) is_image[i] = modes[i] == 0;
-  int rc = time_vectors_unchecked(w->time_in_w1, w->time_in_w2, w->ref_time_in_w1,
-                                  w->ref_time_in_w2, sigma, sigma_next, is_image, n_modes, s.vec,
-                                  s.time_ws, stream);
+  rc = time_vectors_unchecked(w->time_in_w1, w->time_in_w2, w->ref_time_in_w1,
+                              w->ref_time_in_w2, sigma, sigma_next, is_image, n_modes, s.vec,
+                              s.time_ws, stream);
   if (rc) return rc;
   GemvBatch mb{};
   for (int i = 0; i < n_modes; ++i) {
@@ -1015,6 +1144,7 @@ int stack_forward_unchecked(const flux3_model_weights* w, const uint16_t* img, i
   fb.x[0] = s.vec;  // the image mode is always first
   fb.y[0] = s.mod_final;
   launch_gemv(fb, 1, 2 * kHidden, kHidden, true, false, stream);
+  }
 
   // a9: embeddings into the residual stream.
   const uint16_t* inputs[3] = {img, cond, txt};
@@ -1103,7 +1233,7 @@ int stack_forward_unchecked(const flux3_model_weights* w, const uint16_t* img, i
 // bf16 copy of x [n_img][128] the embedding reads.
 size_t sample_ws_bytes(int n_img, int n_cond, int n_txt) {
   return stack_ws_bytes(n_img, n_cond, n_txt) + align256((size_t)n_img * 128 * 4) +
-         align256((size_t)n_img * 128 * 2);
+         align256((size_t)n_img * 128 * 2) + cond_chunk_bytes();
 }
 }  // namespace
 
@@ -1148,12 +1278,24 @@ int flux3_sample(const flux3_model_weights* w, float* x, int n_img, const uint16
   float* v = (float*)p;
   bf16* xb = (bf16*)(p + align256((size_t)n_img * 128 * 4));
   const int n_lat = n_img * 128;
+  char* cond_buf = (char*)xb + align256((size_t)n_img * 128 * 2);
   launch_euler(x, xb, nullptr, n_lat, 0.f, stream);  // xb = bf16(x)
-  for (int k = 0; k < steps; ++k) {
-    rc = stack_forward_unchecked(w, (const uint16_t*)xb, n_img, cond, n_cond, txt, n_txt, table,
-                                 sigmas[k], sigmas[k + 1], v, workspace, stream);
+  // The conditioning depends on the step's sigmas only: computed for up to
+  // kCondChunk steps at a time, each weight read once per launch for them.
+  int modes[3];
+  const int n_modes = present_modes(n_img, n_cond, n_txt, modes, nullptr);
+  CondSlot slots[kCondChunk];
+  for (int k0 = 0; k0 < steps; k0 += kCondChunk) {
+    const int nk = std::min(kCondChunk, steps - k0);
+    rc = precompute_cond(w, modes, n_modes, sigmas, k0, nk, cond_buf, slots, stream);
     if (rc) return rc;
-    launch_euler(x, k + 1 < steps ? xb : nullptr, v, n_lat, sigmas[k + 1] - sigmas[k], stream);
+    for (int j = 0; j < nk; ++j) {
+      const int k = k0 + j;
+      rc = stack_forward_unchecked(w, (const uint16_t*)xb, n_img, cond, n_cond, txt, n_txt, table,
+                                   sigmas[k], sigmas[k + 1], v, workspace, stream, &slots[j]);
+      if (rc) return rc;
+      launch_euler(x, k + 1 < steps ? xb : nullptr, v, n_lat, sigmas[k + 1] - sigmas[k], stream);
+    }
   }
   return check_launch("sample");
 }

@@ -302,6 +302,35 @@ def test_sample_one_call(L):
     assert torch.equal(x, x0)
 
 
+@pytest.mark.parametrize("base", [False, True])
+def test_sample_conditioning_chunks(L, base):
+    """flux3_sample computes the conditioning of up to eight steps at a time:
+    10 steps (a chunk of eight, then two) equal the step-by-step calls bit for
+    bit, with the flow-map checkpoint's ref_time_in and without it."""
+    lay = syn.Layout(4, 4, 8)
+    seed = 330 + int(base)
+    steps = 10
+    wts = Weights(L, seed, lay, 1, 1, base=base)
+    img, _, txt = _inputs(lay, seed)
+    table = L.flux3_rope_table(L.flux3_build_ids(lay.img_h, lay.img_w, lay.n_txt).to("cuda"))
+    sig = L.flux3_sigmas(steps)
+    txt_d = dev(txt)
+    say(f"sample conditioning chunks: {steps} steps, base={base}")
+    x = dev(img).float()
+    ws = L.workspace(L.flux3_sample_workspace_size(lay.n_img, 0, lay.n_txt))
+    L.flux3_sample(wts.model, x, None, txt_d, table, sig, ws)
+    xs, xb = dev(img).float(), dev(img)
+    v = torch.empty((lay.n_img, 128), dtype=torch.float32, device="cuda")
+    sws = L.workspace(L.flux3_stack_workspace_size(lay.n_img, 0, lay.n_txt))
+    s = sig.tolist()
+    for k in range(steps):
+        L.flux3_stack_forward(wts.model, xb, None, txt_d, table, s[k], s[k + 1], v, sws)
+        L.flux3_euler_step(xs, xb, v, s[k], s[k + 1])
+    torch.cuda.synchronize()
+    assert torch.isfinite(x).all()
+    assert torch.equal(x, xs), "flux3_sample differs from the step-by-step loop"
+
+
 def test_sample_graph_replays(L):
     """flux3_sample captured into one HIP graph: every replay (with eager
     library work and synchronisations between replays, sharing the
