@@ -389,6 +389,9 @@ int flux3_euler_step(float* x, uint16_t* x_bf16, const float* v, int n, float si
  *   sigmas : host [steps+1] fp32 (e.g. from flux3_sigmas), all finite
  *   steps  : >= 0 (0 leaves x untouched)
  *   workspace : device, >= flux3_sample_workspace_size(n_img, n_cond, n_txt)
+ * The conditioning vectors (time MLPs, modulations, final adaLN), which
+ * depend on the sigmas only, are computed for up to eight steps at a time
+ * before those steps run, each weight read once per launch for several steps.
  * The result equals steps calls of flux3_stack_forward + flux3_euler_step
  * bit for bit. */
 size_t flux3_sample_workspace_size(int n_img, int n_cond, int n_txt);
