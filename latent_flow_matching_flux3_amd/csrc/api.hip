@@ -1079,14 +1079,15 @@ int precompute_cond(const flux3_model_weights* w, const int* modes, int n_modes,
         r2.add(B(w->ref_time_in_w2), rh + (size_t)j * kHidden, slots[j].vec + (size_t)i * kHidden);
     r2.flush();
   }
-  // modulations: early and single per mode, final adaLN on the image vector
+  // modulations: early and single per mode, final adaLN on the image vector;
+  // weight by weight, so that a launch's items share one weight
   GemvItems mods(3 * kHidden, kHidden, true, false, st);
-  for (int j = 0; j < nk; ++j)
-    for (int i = 0; i < n_modes; ++i) {
-      const float* v = slots[j].vec + (size_t)i * kHidden;
-      mods.add(B(w->early_mod[modes[i]]), v, slots[j].mod_early + (size_t)i * 3 * kHidden);
-      mods.add(B(w->single_mod[modes[i]]), v, slots[j].mod_single + (size_t)i * 3 * kHidden);
-    }
+  for (int i = 0; i < n_modes; ++i)
+    for (int single = 0; single < 2; ++single)
+      for (int j = 0; j < nk; ++j)
+        mods.add(B(single ? w->single_mod[modes[i]] : w->early_mod[modes[i]]),
+                 slots[j].vec + (size_t)i * kHidden,
+                 (single ? slots[j].mod_single : slots[j].mod_early) + (size_t)i * 3 * kHidden);
   mods.flush();
   GemvItems fin(2 * kHidden, kHidden, true, false, st);
   for (int j = 0; j < nk; ++j) fin.add(B(w->final_ada), slots[j].vec, slots[j].mod_final);
